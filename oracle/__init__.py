@@ -1,0 +1,164 @@
+"""CPU oracle for the DeepSeek Sparse Attention hot path.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` are the only callers.  The GPU library never
+imports, links or calls this package, and this package imports nothing from it.
+
+The arithmetic lives in ``dsa_oracle.c`` (plain C, OpenMP over query rows,
+double precision); this module only builds it with gcc and marshals numpy
+arrays.  Every function works on an explicit list of query rows, given by batch
+index and absolute position, so large workloads can be checked on a sample.
+
+Sources (cited by page title and section):
+  * "DeepSeek V3.2 and the lightning indexer", section "How the lightning
+    indexer works": indexer heads, weighted sum of ReLU'd dot products, FP8,
+    top-2048 per query, MQA mode of MLA with one selection per query position.
+  * DeepSeek-V3.2 spec sheet, design overview and section 2.1: every
+    preceding token is scored; fine-grained top-k; MQA-mode MLA latents.
+Readings where the pages are silent are listed in the module docstrings of the
+functions below.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> None:
+    src = os.path.join(_HERE, "dsa_oracle.c")
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+                           src, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+        L.dsa_oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+        L.dsa_oracle_e4m3_to_double.restype = ctypes.c_double
+        L.dsa_oracle_index_scores.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, vp, vp]
+        L.dsa_oracle_index_scores.restype = None
+        L.dsa_oracle_topk.argtypes = [i32, i32, i64, vp, vp, vp]
+        L.dsa_oracle_topk.restype = None
+        L.dsa_oracle_sparse_mla_attn.argtypes = [i32, i32, i32, i32, i32, f32, i64,
+                                                 vp, vp, vp, vp, vp, vp]
+        L.dsa_oracle_sparse_mla_attn.restype = None
+        L.dsa_oracle_max_threads.argtypes = []
+        L.dsa_oracle_max_threads.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def max_threads() -> int:
+    return int(lib().dsa_oracle_max_threads())
+
+
+def e4m3_to_float64(codes) -> np.ndarray:
+    """OCP FP8 e4m3fn byte -> value, from the format's definition."""
+    codes = np.asarray(codes, dtype=np.uint8).ravel()
+    f = lib().dsa_oracle_e4m3_to_double
+    return np.array([f(int(c)) for c in codes], dtype=np.float64)
+
+
+def index_scores(k_idx, q_idx_rows, w_rows, row_batch, row_pos, fill=np.nan) -> np.ndarray:
+    """Lightning-indexer scores of the given query rows.
+
+    k_idx      [B, Lk, d_I] uint8 (e4m3fn)
+    q_idx_rows [R, H_I, d_I] uint8 (e4m3fn)
+    w_rows     [R, H_I] float32
+    row_batch, row_pos  [R] int32 (absolute position pos(t) = q_start + t)
+    Returns [R, Lk] float32 with I[r, s] for s <= pos_r and `fill` elsewhere.
+    Causal set reading: s ranges over 0..pos(t) inclusive of the query's own
+    token ("every preceding token" read inclusively, so the first token has a
+    candidate and dense-equivalence at L <= k is standard causal attention).
+    """
+    k_idx = np.ascontiguousarray(k_idx, dtype=np.uint8)
+    B, Lk, dI = k_idx.shape
+    q_idx_rows, qp = _c(q_idx_rows, np.uint8)
+    R, HI, dI2 = q_idx_rows.shape
+    assert dI2 == dI
+    w_rows, wp = _c(w_rows, np.float32)
+    assert w_rows.shape == (R, HI)
+    rb, rbp = _c(row_batch, np.int32)
+    rp, rpp = _c(row_pos, np.int32)
+    assert rb.shape == (R,) and rp.shape == (R,)
+    assert (rb >= 0).all() and (rb < B).all() and (rp >= 0).all()
+    out = np.full((R, Lk), fill, dtype=np.float32)
+    lib().dsa_oracle_index_scores(Lk, HI, dI, R, rbp, rpp, qp, wp, k_idx.ctypes.data, out.ctypes.data)
+    return out
+
+
+def topk(scores_rows, row_pos, k: int) -> np.ndarray:
+    """Top-k selection per row over candidates s <= pos_r.
+
+    Order (score desc, index asc): ties go to the lower index (reading: the
+    pages do not say).  Output [R, k] int32 ascending, padded with -1 when the
+    row has fewer than k candidates.
+    """
+    scores_rows, sp = _c(scores_rows, np.float32)
+    R, Lk = scores_rows.shape
+    rp, rpp = _c(row_pos, np.int32)
+    assert rp.shape == (R,)
+    out = np.empty((R, k), dtype=np.int32)
+    lib().dsa_oracle_topk(Lk, k, R, rpp, sp, out.ctypes.data)
+    return out
+
+
+def sparse_mla_attn(kv, q_rows, indices, row_batch, d_latent: int, softmax_scale: float):
+    """Sparse MQA-mode attention over the selected latents, in double precision.
+
+    kv      [B, Lk, D_v + D_r] uint16 (bf16 bits)
+    q_rows  [R, H, D_v + D_r] uint16 (bf16 bits)
+    indices [R, k] int32 (entries outside [0, Lk) are skipped)
+    Value = the first d_latent columns of each latent row (reading of
+    "value dim taken from the latent").  Returns (out [R, H, D_v] float32,
+    lse [R, H] float32).
+    """
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    B, Lk, Dqk = kv.shape
+    q_rows, qp = _c(q_rows, np.uint16)
+    R, H, Dqk2 = q_rows.shape
+    assert Dqk2 == Dqk and 0 < d_latent <= Dqk
+    indices, ip = _c(indices, np.int32)
+    assert indices.shape[0] == R
+    k = indices.shape[1]
+    rb, rbp = _c(row_batch, np.int32)
+    assert (rb >= 0).all() and (rb < B).all()
+    out = np.empty((R, H, d_latent), dtype=np.float32)
+    lse = np.empty((R, H), dtype=np.float32)
+    lib().dsa_oracle_sparse_mla_attn(Lk, H, d_latent, Dqk - d_latent, k, float(softmax_scale), R,
+                                     rbp, qp, kv.ctypes.data, ip, out.ctypes.data, lse.ctypes.data)
+    return out, lse
+
+
+def forward(k_idx, q_idx_rows, w_rows, q_rows, kv, row_batch, row_pos, k: int, d_latent: int,
+            softmax_scale: float):
+    """Indexer -> top-k -> sparse attention for the given rows.
+    Returns dict(scores, indices, out, lse, seconds)."""
+    t0 = time.perf_counter()
+    s = index_scores(k_idx, q_idx_rows, w_rows, row_batch, row_pos)
+    t1 = time.perf_counter()
+    idx = topk(s, row_pos, k)
+    t2 = time.perf_counter()
+    out, lse = sparse_mla_attn(kv, q_rows, idx, row_batch, d_latent, softmax_scale)
+    t3 = time.perf_counter()
+    return dict(scores=s, indices=idx, out=out, lse=lse,
+                seconds=dict(index=t1 - t0, topk=t2 - t1, attn=t3 - t2, total=t3 - t0))

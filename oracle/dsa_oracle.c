@@ -1,0 +1,204 @@
+/*
+ * CPU oracle for the DeepSeek Sparse Attention (DSA) hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the GPU library and includes nothing from it.
+ *
+ * It evaluates the plain definitions, slowly and in wide arithmetic:
+ *
+ *  - Lightning indexer ("DeepSeek V3.2 and the lightning indexer", section
+ *    "How the lightning indexer works"; DeepSeek-V3.2 spec sheet, design
+ *    overview / section 2.1): a few indexer heads score the query against each
+ *    preceding token as a weighted sum of ReLU-activated dot products, in FP8:
+ *        I[t,s] = sum_j w[t,j] * ReLU(q_I[t,j,:] . k_I[s,:]),  s <= pos(t).
+ *    Every FP8 e4m3 value is an integer multiple of 2^-9 with at most 4
+ *    significant bits, so each dot product over d_I <= 2^10 terms is exact in
+ *    double precision.  The weighted head sum is accumulated in double and
+ *    rounded once to fp32; it is exact whenever the terms w * ReLU(.) need at
+ *    most 53 bits, which always holds on the 0.25-step input grids.  The
+ *    accumulator starts at +0, so the result is never -0.
+ *  - Top-k (same sections): each query keeps its k best-scoring preceding
+ *    tokens.  Ties go to the lower token index, the kept indices are written
+ *    in ascending order, and unused slots hold -1 (readings of points the
+ *    pages leave open).
+ *  - Sparse attention in the MQA mode of MLA (lightning-indexer post, same
+ *    section: one latent per token, shared by all query heads, selection made
+ *    once per query position): softmax attention of every query head over the
+ *    selected latents only, in double precision; the value is the first
+ *    d_latent columns of each latent row and the scores use all
+ *    d_latent + d_rope columns.
+ *
+ * Query rows are given explicitly (batch index, absolute position and the
+ * row's own query data), so any subset of a workload's rows can be evaluated.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------------
+ * Number formats
+ * ------------------------------------------------------------------------- */
+
+/* OCP FP8 e4m3fn: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0;
+ * exponent 0 encodes subnormals m * 2^-9; S.1111.111 is NaN; no infinities. */
+double dsa_oracle_e4m3_to_double(uint8_t code) {
+  const int sign = code >> 7;
+  const int e = (code >> 3) & 0xF;
+  const int m = code & 0x7;
+  if (e == 15 && m == 7) return NAN;
+  const double mag = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return sign ? -mag : mag;
+}
+
+/* bfloat16: the top 16 bits of an IEEE binary32. */
+static double bf16_to_double(uint16_t bits) {
+  const uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ---------------------------------------------------------------------------
+ * Lightning indexer
+ * ------------------------------------------------------------------------- */
+
+/* scores[r, s] for s in [0, min(pos_r, Lk-1)]; other entries are untouched.
+ *   q_idx_rows [nrows, H_I, d_I] e4m3fn, w_rows [nrows, H_I] fp32,
+ *   k_idx [B, Lk, d_I] e4m3fn, scores [nrows, Lk] fp32. */
+void dsa_oracle_index_scores(int32_t kv_len, int32_t idx_heads, int32_t idx_dim, int64_t nrows,
+                             const int32_t* row_batch, const int32_t* row_pos,
+                             const uint8_t* q_idx_rows, const float* w_rows,
+                             const uint8_t* k_idx, float* scores) {
+  double table[256];
+  for (int c = 0; c < 256; ++c) table[c] = dsa_oracle_e4m3_to_double((uint8_t)c);
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const uint8_t* keys = k_idx + (int64_t)row_batch[r] * kv_len * idx_dim;
+    const uint8_t* qr = q_idx_rows + r * idx_heads * idx_dim;
+    const float* wr = w_rows + r * idx_heads;
+    const int64_t last = row_pos[r] < kv_len - 1 ? row_pos[r] : kv_len - 1;
+    for (int64_t s = 0; s <= last; ++s) {
+      const uint8_t* ks = keys + s * idx_dim;
+      double score = 0.0;
+      for (int j = 0; j < idx_heads; ++j) {
+        const uint8_t* qj = qr + (int64_t)j * idx_dim;
+        double dot = 0.0;
+        for (int d = 0; d < idx_dim; ++d) dot += table[qj[d]] * table[ks[d]];
+        const double relu = dot > 0.0 ? dot : 0.0;
+        score += (double)wr[j] * relu;
+      }
+      scores[r * kv_len + s] = (float)score;
+    }
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * Top-k
+ * ------------------------------------------------------------------------- */
+
+typedef struct { float score; int32_t index; } cand_t;
+
+/* Order: higher score first; equal scores -> lower index first. */
+static int by_score_then_index(const void* a, const void* b) {
+  const cand_t* x = (const cand_t*)a;
+  const cand_t* y = (const cand_t*)b;
+  if (x->score > y->score) return -1;
+  if (x->score < y->score) return 1;
+  return (x->index > y->index) - (x->index < y->index);
+}
+
+static int by_index(const void* a, const void* b) {
+  const int32_t x = *(const int32_t*)a, y = *(const int32_t*)b;
+  return (x > y) - (x < y);
+}
+
+/* indices[r, :] = the min(k, pos_r + 1) best candidates s <= pos_r of row r,
+ * ascending, padded with -1.  scores [nrows, Lk] fp32 (only s <= pos_r read). */
+void dsa_oracle_topk(int32_t kv_len, int32_t topk, int64_t nrows, const int32_t* row_pos,
+                     const float* scores, int32_t* indices) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t n = (row_pos[r] < kv_len - 1 ? row_pos[r] : kv_len - 1) + 1;
+    int32_t* out = indices + r * topk;
+    const int64_t keep = n < topk ? n : topk;
+    cand_t* c = (cand_t*)malloc((size_t)n * sizeof(cand_t));
+    for (int64_t s = 0; s < n; ++s) {
+      c[s].score = scores[r * kv_len + s];
+      c[s].index = (int32_t)s;
+    }
+    qsort(c, (size_t)n, sizeof(cand_t), by_score_then_index);
+    for (int64_t i = 0; i < keep; ++i) out[i] = c[i].index;
+    qsort(out, (size_t)keep, sizeof(int32_t), by_index);
+    for (int64_t i = keep; i < topk; ++i) out[i] = -1;
+    free(c);
+  }
+}
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention, MQA mode of MLA
+ * ------------------------------------------------------------------------- */
+
+/* For each row r and head h, over the selected tokens s (entries of
+ * indices[r, :] that lie in [0, Lk); -1 and out-of-range entries are skipped):
+ *   z_s   = scale * sum_{d < D_v + D_r} q[r,h,d] * kv[b_r, s, d]
+ *   p_s   = exp(z_s - max z) / Z,   Z = sum exp(z_s - max z)
+ *   out   = sum_s p_s * kv[b_r, s, 0:D_v]
+ *   lse   = max z + ln Z
+ * A row with no selected token gives out = 0 and lse = -inf.
+ *   q_rows [nrows, H, D_v+D_r] bf16, kv [B, Lk, D_v+D_r] bf16,
+ *   indices [nrows, k] int32, out [nrows, H, D_v] fp32, lse [nrows, H] fp32 (nullable). */
+void dsa_oracle_sparse_mla_attn(int32_t kv_len, int32_t heads, int32_t d_latent, int32_t d_rope,
+                                int32_t topk, float softmax_scale, int64_t nrows,
+                                const int32_t* row_batch, const uint16_t* q_rows,
+                                const uint16_t* kv, const int32_t* indices, float* out,
+                                float* lse) {
+  const int32_t dqk = d_latent + d_rope;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int64_t r = 0; r < nrows; ++r) {
+    for (int32_t h = 0; h < heads; ++h) {
+      const uint16_t* cache = kv + (int64_t)row_batch[r] * kv_len * dqk;
+      const int32_t* sel = indices + r * topk;
+      double* z = (double*)malloc((size_t)topk * sizeof(double));
+      double* acc = (double*)calloc((size_t)d_latent, sizeof(double));
+      double* qh = (double*)malloc((size_t)dqk * sizeof(double));
+      for (int d = 0; d < dqk; ++d) qh[d] = bf16_to_double(q_rows[(r * heads + h) * dqk + d]);
+      double zmax = -INFINITY;
+      for (int i = 0; i < topk; ++i) {
+        const int32_t s = sel[i];
+        if (s < 0 || s >= kv_len) { z[i] = -INFINITY; continue; }
+        const uint16_t* row = cache + (int64_t)s * dqk;
+        double dot = 0.0;
+        for (int d = 0; d < dqk; ++d) dot += qh[d] * bf16_to_double(row[d]);
+        z[i] = (double)softmax_scale * dot;
+        if (z[i] > zmax) zmax = z[i];
+      }
+      double Z = 0.0;
+      for (int i = 0; i < topk; ++i) {
+        const int32_t s = sel[i];
+        if (s < 0 || s >= kv_len) continue;
+        const double p = exp(z[i] - zmax);
+        Z += p;
+        const uint16_t* row = cache + (int64_t)s * dqk;
+        for (int d = 0; d < d_latent; ++d) acc[d] += p * bf16_to_double(row[d]);
+      }
+      float* o = out + (r * heads + h) * d_latent;
+      for (int d = 0; d < d_latent; ++d) o[d] = Z > 0.0 ? (float)(acc[d] / Z) : 0.0f;
+      if (lse) lse[r * heads + h] = Z > 0.0 ? (float)(zmax + log(Z)) : -INFINITY;
+      free(qh);
+      free(z);
+      free(acc);
+    }
+  }
+}
+
+int dsa_oracle_max_threads(void) {
+#ifdef _OPENMP
+  extern int omp_get_max_threads(void);
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
