@@ -1,0 +1,165 @@
+/*
+ * dsa.h — C ABI of libdsa.so, the DeepSeek Sparse Attention (DSA) hot path on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The path has three stages, each its own entry point, plus a fused forward:
+ *
+ *   dsa_index_scores     lightning indexer: a few indexer heads score every
+ *                        (query, preceding token) pair as a weighted sum of
+ *                        ReLU'd FP8 dot products.
+ *                        ("DeepSeek V3.2 and the lightning indexer", section
+ *                        "How the lightning indexer works"; DeepSeek-V3.2 spec
+ *                        sheet, design overview / section 2.1.)
+ *   dsa_topk             fine-grained token selection: each query keeps the k
+ *                        best-scoring preceding tokens (same sections; k = 2048
+ *                        in the sparse training stage).
+ *   dsa_sparse_mla_attn  MLA in its MQA mode over the selected latents only:
+ *                        one latent vector per token, shared by every query
+ *                        head, one selection per query position (lightning
+ *                        indexer post, same section; spec sheet, "Inference
+ *                        efficiency" table, KV-cache design).
+ *   dsa_forward          the three stages in order on one stream.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer to a dense row-major buffer that
+ *    the caller allocates and owns.  The library never allocates, frees or
+ *    retains device memory and keeps no state between calls.  Buffers must
+ *    stay alive until the stream work completes.  Outputs must not alias
+ *    inputs.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work and return; kernel faults surface at the caller's next
+ *    synchronisation.
+ *  - Shapes: B = batch, Lq = new query tokens per sequence, Lk = cached tokens
+ *    per sequence, H_I = indexer heads, d_I = indexer dim, H = query heads,
+ *    D_v = latent (= value) width, D_r = rope width, D_qk = D_v + D_r.
+ *    Query row t of sequence b sits at absolute position pos(t) = q_start + t
+ *    and may look at tokens s = 0 .. pos(t) (its own token included).
+ *  - Return value: DSA_OK (0) or a negative status.  Every argument check runs
+ *    before any launch, so a call that fails leaves every buffer untouched.
+ *    dsa_last_error() gives a thread-local description of the last failure.
+ *  - There is no CPU fallback: shapes the kernels do not cover return
+ *    DSA_ERR_UNSUPPORTED.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  DSA_ERR_SHAPE = -2,       /* non-positive size, q_start+q_len > kv_len, bad scale */
+  DSA_ERR_UNSUPPORTED = -3, /* a size the kernels do not cover                    */
+  DSA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required         */
+  DSA_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                    */
+  DSA_ERR_HIP = -6          /* the HIP runtime rejected a launch                   */
+};
+
+/* Problem description.  All fields are read by every entry point that needs
+ * them; unused fields are ignored (e.g. heads/d_latent by dsa_index_scores). */
+typedef struct dsa_problem {
+  int32_t batch;       /* B  >= 1                                              */
+  int32_t q_len;       /* Lq >= 1                                              */
+  int32_t kv_len;      /* Lk >= 1, q_start + q_len <= kv_len                    */
+  int32_t q_start;     /* absolute position of query row 0 (>= 0)              */
+  int32_t idx_heads;   /* H_I, 1..64                                           */
+  int32_t idx_dim;     /* d_I, multiple of 16, 16..128                         */
+  int32_t topk;        /* k, 1..2048                                           */
+  int32_t heads;       /* H, 1..128                                            */
+  int32_t d_latent;    /* D_v: 512, or 64 (with D_r = 16)                       */
+  int32_t d_rope;      /* D_r: 64 (with D_v = 512), or 16 (with D_v = 64)       */
+  float softmax_scale; /* finite, > 0; e.g. 1/sqrt(D_qk)                       */
+} dsa_problem;
+
+/* Operation selector for dsa_workspace_size(). */
+enum dsa_op { DSA_OP_INDEX_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA_ATTN = 2, DSA_OP_FORWARD = 3 };
+
+/*
+ * Lightning indexer scores.
+ *   I[b,t,s] = sum_{j<H_I} w[b,t,j] * ReLU( sum_{d<d_I} q_idx[b,t,j,d] * k_idx[b,s,d] )
+ * for s = 0 .. pos(t); entries with s > pos(t) are NOT written.
+ *
+ *   q_idx  [B, Lq, H_I, d_I] uint8, OCP FP8 e4m3fn (scale 1)
+ *   k_idx  [B, Lk, d_I]      uint8, OCP FP8 e4m3fn, one key per token shared by
+ *                             every indexer head
+ *   w      [B, Lq, H_I]      float32 head weights
+ *   scores [B, Lq, Lk]       float32 output, row stride Lk
+ * The dot products run on FP8 matrix cores with fp32 accumulation; the ReLU
+ * and the weighted head sum in fp32.  Zero results are +0.  When every partial
+ * sum is exactly representable in fp32 (true for the 0.25-step value grids of
+ * [-4,4] for q/k and [-1,1] for w) the result equals the exact value.
+ */
+int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx,
+                     const float* w, float* scores, void* stream);
+
+/*
+ * Top-k selection per query row.
+ * Row (b,t) keeps the min(k, pos(t)+1) candidates s in 0..pos(t) that come
+ * first under the order (score descending, index ascending) — ties go to the
+ * lower index, and -0 equals +0.  Indices are written in ascending order; the
+ * remaining slots hold -1.  Scores at s > pos(t) are never read.  NaN scores
+ * give an unspecified (but in-range) selection.
+ *
+ *   scores  [B, Lq, Lk] float32 (as written by dsa_index_scores)
+ *   indices [B, Lq, k]  int32 output
+ *   workspace: device scratch of at least dsa_workspace_size(p, DSA_OP_TOPK)
+ *              bytes (may be NULL when that size is 0).
+ */
+int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/*
+ * Sparse attention, MQA mode of MLA, over the selected latents.
+ * For every (b, t, h), over the entries s of indices[b,t,:] with 0 <= s < Lk
+ * (other entries, e.g. the -1 padding, are skipped):
+ *   z_s = softmax_scale * sum_{d<D_qk} q[b,t,h,d] * kv[b,s,d]
+ *   out[b,t,h,:] = sum_s softmax(z)_s * kv[b,s,0:D_v]
+ *   lse[b,t,h]   = log(sum_s exp(z_s))             (natural log)
+ * The value of a latent is its first D_v columns; the last D_r columns (rope)
+ * only enter the scores.  A row with no valid entry gives out = 0, lse = -inf.
+ *
+ *   q       [B, Lq, H, D_qk] bfloat16 (raw bits)
+ *   kv      [B, Lk, D_qk]    bfloat16 latent cache, one row per token shared
+ *                             by every head
+ *   indices [B, Lq, k]       int32
+ *   out     [B, Lq, H, D_v]  float32 output
+ *   lse     [B, Lq, H]       float32 output, or NULL
+ * Scores and the softmax run in fp32; the probabilities are rounded to bf16
+ * for the value product on bf16 matrix cores with fp32 accumulation.
+ */
+int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                        const int32_t* indices, float* out, float* lse, void* stream);
+
+/*
+ * dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.
+ * The scores live in the workspace (at least dsa_workspace_size(p,
+ * DSA_OP_FORWARD) bytes, 256-byte aligned).  `indices` may be NULL; when given
+ * ([B, Lq, k] int32) it receives the selection, otherwise the selection is
+ * kept in the workspace.  Results are bit-identical to the three separate
+ * calls.
+ */
+int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace `op` needs for problem `p` (0 if none); returns
+ * (size_t)-1 when the problem is invalid (dsa_last_error() says why). */
+size_t dsa_workspace_size(const dsa_problem* p, int op);
+
+/* Static text for a status code. */
+const char* dsa_status_string(int status);
+
+/* Thread-local text describing the last failing call on this thread. */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,164 @@
+"""Python binding of libdsa.so — the DeepSeek Sparse Attention hot path on MI355X.
+
+Argument marshalling only: every function passes raw device pointers of torch
+tensors and the current HIP stream to the C ABI declared in include/dsa.h and
+raises DsaError on a non-zero status.  All computation happens in the HIP
+kernels; there is no CPU fallback, and importing this module fails loudly when
+the built library is missing (build it with ``python -m
+sparse_attention_02_amd.build`` or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+DSA_OP_INDEX_SCORES, DSA_OP_TOPK, DSA_OP_SPARSE_MLA_ATTN, DSA_OP_FORWARD = 0, 1, 2, 3
+STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_UNSUPPORTED",
+          -4: "DSA_ERR_WORKSPACE", -5: "DSA_ERR_ALIGN", -6: "DSA_ERR_HIP"}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "q_len", "kv_len", "q_start", "idx_heads", "idx_dim", "topk",
+                 "heads", "d_latent", "d_rope")] + [("softmax_scale", ctypes.c_float)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Problem:
+    """Mirror of struct dsa_problem (include/dsa.h)."""
+    batch: int
+    q_len: int
+    kv_len: int
+    q_start: int
+    idx_heads: int
+    idx_dim: int
+    topk: int
+    heads: int
+    d_latent: int
+    d_rope: int
+    softmax_scale: Optional[float] = None
+
+    def c(self) -> _Problem:
+        scale = self.softmax_scale
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.d_latent + self.d_rope)
+        return _Problem(self.batch, self.q_len, self.kv_len, self.q_start, self.idx_heads,
+                        self.idx_dim, self.topk, self.heads, self.d_latent, self.d_rope, scale)
+
+    @classmethod
+    def from_workload(cls, wl) -> "Problem":
+        return cls(wl.batch, wl.q_len, wl.kv_len, wl.q_start, wl.idx_heads, wl.idx_dim,
+                   wl.topk, wl.heads, wl.d_latent, wl.d_rope, wl.softmax_scale)
+
+
+def _load():
+    # torch ships its own HIP runtime with the same soname as the system one.
+    # Import it first so libdsa.so binds to the runtime that owns torch's
+    # device memory and streams (loading libdsa.so first would pull the system
+    # runtime into the process and leave torch on a mismatched stack).
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_attention_02_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(_Problem)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    L.dsa_index_scores.argtypes = [P, vp, vp, vp, vp, vp]
+    L.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_forward):
+        f.restype = i32
+    L.dsa_workspace_size.argtypes = [P, i32]
+    L.dsa_workspace_size.restype = sz
+    L.dsa_status_string.argtypes = [i32]
+    L.dsa_status_string.restype = ctypes.c_char_p
+    L.dsa_last_error.argtypes = []
+    L.dsa_last_error.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsaError(status, lib.dsa_last_error().decode())
+
+
+def workspace_size(problem: Problem, op: int) -> int:
+    n = lib.dsa_workspace_size(ctypes.byref(problem.c()), op)
+    if n == ctypes.c_size_t(-1).value:
+        raise DsaError(-2, lib.dsa_last_error().decode())
+    return n
+
+
+def dsa_index_scores(problem: Problem, q_idx, k_idx, w, scores, stream=None) -> None:
+    """scores[b,t,s] for s <= pos(t) (include/dsa.h: dsa_index_scores)."""
+    _check(lib.dsa_index_scores(ctypes.byref(problem.c()), _ptr(q_idx), _ptr(k_idx), _ptr(w),
+                                _ptr(scores), _stream(stream)))
+
+
+def dsa_topk(problem: Problem, scores, indices, workspace=None, workspace_bytes: int = 0,
+             stream=None) -> None:
+    """indices[b,t,:] = ascending top-k of row (b,t), -1 padded (include/dsa.h: dsa_topk)."""
+    if workspace is not None and not isinstance(workspace, int) and workspace_bytes == 0:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dsa_topk(ctypes.byref(problem.c()), _ptr(scores), _ptr(indices), _ptr(workspace),
+                        workspace_bytes, _stream(stream)))
+
+
+def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:
+    """Sparse MQA-mode attention over the selected latents (include/dsa.h: dsa_sparse_mla_attn)."""
+    _check(lib.dsa_sparse_mla_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
+                                   _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def dsa_forward(problem: Problem, q_idx, k_idx, w, q, kv, out, lse=None, indices=None,
+                workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    """Indexer -> top-k -> sparse attention on one stream (include/dsa.h: dsa_forward)."""
+    if workspace is not None and not isinstance(workspace, int) and workspace_bytes == 0:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dsa_forward(ctypes.byref(problem.c()), _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q),
+                           _ptr(kv), _ptr(out), _ptr(lse), _ptr(indices), _ptr(workspace),
+                           workspace_bytes, _stream(stream)))
+
+
+def dsa_workspace_size(problem: Problem, op: int) -> int:
+    return workspace_size(problem, op)
+
+
+def dsa_last_error() -> str:
+    return lib.dsa_last_error().decode()
+
+
+def dsa_status_string(status: int) -> str:
+    return lib.dsa_status_string(status).decode()

@@ -1,0 +1,232 @@
+// C ABI of libdsa.so: argument checks, workspace layout and kernel launches.
+// The entry points and their contracts are declared in include/dsa.h.
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+int check_common(const dsa_problem* p) {
+  if (!p) return fail(DSA_ERR_NULL, "problem is NULL");
+  if (p->batch < 1 || p->q_len < 1 || p->kv_len < 1 || p->q_start < 0)
+    return fail(DSA_ERR_SHAPE, "batch, q_len, kv_len must be >= 1 and q_start >= 0 (got %d, %d, %d, %d)",
+                p->batch, p->q_len, p->kv_len, p->q_start);
+  if ((long long)p->q_start + p->q_len > p->kv_len)
+    return fail(DSA_ERR_SHAPE, "q_start + q_len (%lld) exceeds kv_len (%d)",
+                (long long)p->q_start + p->q_len, p->kv_len);
+  if ((long long)p->batch * p->q_len > 0x7FFFFFFFLL)
+    return fail(DSA_ERR_UNSUPPORTED, "batch * q_len exceeds 2^31 - 1");
+  return DSA_OK;
+}
+
+int check_index(const dsa_problem* p) {
+  if (p->idx_heads < 1 || p->idx_dim < 1)
+    return fail(DSA_ERR_SHAPE, "idx_heads and idx_dim must be >= 1");
+  if (p->idx_heads > 64) return fail(DSA_ERR_UNSUPPORTED, "idx_heads %d > 64", p->idx_heads);
+  if (p->idx_dim % 32 != 0 || p->idx_dim > 128)
+    return fail(DSA_ERR_UNSUPPORTED, "idx_dim %d: supported 32, 64, 96, 128", p->idx_dim);
+  return DSA_OK;
+}
+
+int check_topk(const dsa_problem* p) {
+  if (p->topk < 1) return fail(DSA_ERR_SHAPE, "topk must be >= 1");
+  if (p->topk > 2048) return fail(DSA_ERR_UNSUPPORTED, "topk %d > 2048", p->topk);
+  return DSA_OK;
+}
+
+int check_attn(const dsa_problem* p) {
+  if (int s = check_topk(p)) return s;
+  if (p->heads < 1 || p->d_latent < 1 || p->d_rope < 0)
+    return fail(DSA_ERR_SHAPE, "heads, d_latent must be >= 1 and d_rope >= 0");
+  if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be finite and > 0");
+  if (p->heads > 128) return fail(DSA_ERR_UNSUPPORTED, "heads %d > 128", p->heads);
+  const bool mla = p->d_latent == 512 && p->d_rope == 64;
+  const bool tiny = p->d_latent == 64 && p->d_rope == 16;
+  if (!mla && !tiny)
+    return fail(DSA_ERR_UNSUPPORTED, "latent shape %d + %d: supported 512 + 64 and 64 + 16",
+                p->d_latent, p->d_rope);
+  return DSA_OK;
+}
+
+int check_ptr(const void* ptr, const char* name, size_t align) {
+  if (!ptr) return fail(DSA_ERR_NULL, "%s is NULL", name);
+  if (!aligned(ptr, align)) return fail(DSA_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return DSA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t scores_bytes(const dsa_problem* p) {
+  return (size_t)p->batch * p->q_len * p->kv_len * sizeof(float);
+}
+size_t indices_bytes(const dsa_problem* p) {
+  return (size_t)p->batch * p->q_len * p->topk * sizeof(int32_t);
+}
+
+dsa::IndexArgs index_args(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx,
+                          const float* w, float* scores) {
+  dsa::IndexArgs a{};
+  a.q_idx = q_idx; a.k_idx = k_idx; a.w = w; a.scores = scores;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start;
+  a.HI = p->idx_heads; a.dI = p->idx_dim;
+  return a;
+}
+
+dsa::TopkArgs topk_args(const dsa_problem* p, const float* scores, int32_t* indices) {
+  dsa::TopkArgs a{};
+  a.scores = scores; a.indices = indices;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start; a.k = p->topk;
+  return a;
+}
+
+dsa::AttnArgs attn_args(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                        const int32_t* indices, float* out, float* lse) {
+  dsa::AttnArgs a{};
+  a.q = q; a.kv = kv; a.indices = indices; a.out = out; a.lse = lse;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.H = p->heads;
+  a.Dv = p->d_latent; a.Dr = p->d_rope; a.k = p->topk;
+  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "null pointer";
+    case DSA_ERR_SHAPE: return "invalid shape or scale";
+    case DSA_ERR_UNSUPPORTED: return "unsupported size";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_ALIGN: return "misaligned pointer";
+    case DSA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error; }
+
+size_t dsa_workspace_size(const dsa_problem* p, int op) {
+  const size_t bad = (size_t)-1;
+  if (check_common(p)) return bad;
+  switch (op) {
+    case DSA_OP_INDEX_SCORES:
+      return check_index(p) ? bad : 0;
+    case DSA_OP_TOPK:
+      if (check_topk(p)) return bad;
+      return dsa::topk_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk);
+    case DSA_OP_SPARSE_MLA_ATTN:
+      return check_attn(p) ? bad : 0;
+    case DSA_OP_FORWARD:
+      if (check_index(p) || check_attn(p)) return bad;
+      return round_up(scores_bytes(p)) + round_up(indices_bytes(p)) +
+             round_up(dsa::topk_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk));
+    default:
+      fail(DSA_ERR_SHAPE, "unknown op %d", op);
+      return bad;
+  }
+}
+
+int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx,
+                     const float* w, float* scores, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_index(p)) return s;
+  if (int s = check_ptr(q_idx, "q_idx", 16)) return s;
+  if (int s = check_ptr(k_idx, "k_idx", 16)) return s;
+  if (int s = check_ptr(w, "w", 4)) return s;
+  if (int s = check_ptr(scores, "scores", 4)) return s;
+  return hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores),
+                                             (hipStream_t)stream),
+                    "index_scores launch");
+}
+
+int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_topk(p)) return s;
+  if (int s = check_ptr(scores, "scores", 4)) return s;
+  if (int s = check_ptr(indices, "indices", 4)) return s;
+  const size_t need = dsa::topk_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  return hip_status(dsa::launch_topk(topk_args(p, scores, indices), (hipStream_t)stream),
+                    "topk launch");
+}
+
+int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                        const int32_t* indices, float* out, float* lse, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_attn(p)) return s;
+  if (int s = check_ptr(q, "q", 16)) return s;
+  if (int s = check_ptr(kv, "kv", 16)) return s;
+  if (int s = check_ptr(indices, "indices", 16)) return s;
+  if (int s = check_ptr(out, "out", 16)) return s;
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_ALIGN, "lse is not 4-byte aligned");
+  return hip_status(dsa::launch_sparse_mla_attn(attn_args(p, q, kv, indices, out, lse),
+                                                (hipStream_t)stream),
+                    "sparse_mla_attn launch");
+}
+
+int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_index(p)) return s;
+  if (int s = check_attn(p)) return s;
+  if (int s = check_ptr(q_idx, "q_idx", 16)) return s;
+  if (int s = check_ptr(k_idx, "k_idx", 16)) return s;
+  if (int s = check_ptr(w, "w", 4)) return s;
+  if (int s = check_ptr(q, "q", 16)) return s;
+  if (int s = check_ptr(kv, "kv", 16)) return s;
+  if (int s = check_ptr(out, "out", 16)) return s;
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (indices && !aligned(indices, 16)) return fail(DSA_ERR_ALIGN, "indices is not 16-byte aligned");
+  const size_t need = dsa_workspace_size(p, DSA_OP_FORWARD);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  if (!aligned(workspace, kAlign)) return fail(DSA_ERR_ALIGN, "workspace is not 256-byte aligned");
+
+  uint8_t* ws = (uint8_t*)workspace;
+  float* scores = (float*)ws;
+  int32_t* sel = indices ? indices : (int32_t*)(ws + round_up(scores_bytes(p)));
+  void* topk_ws = ws + round_up(scores_bytes(p)) + round_up(indices_bytes(p));
+  hipStream_t st = (hipStream_t)stream;
+
+  if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
+                         "index_scores launch"))
+    return s;
+  (void)topk_ws;
+  if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel), st), "topk launch")) return s;
+  return hip_status(dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse), st),
+                    "sparse_mla_attn launch");
+}
+
+}  // extern "C"

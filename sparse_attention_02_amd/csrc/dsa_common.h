@@ -1,0 +1,55 @@
+// Device-side helpers shared by the DSA kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// D(16x16, fp32) = A(16x128, e4m3) * B(128x16, e4m3) + C.
+// Operand layout (checked on gfx950): lane l holds row (A) / column (B) l%16 and
+// the 32 consecutive k-bytes [32*(l/16), 32*(l/16)+32).  Result: lane l, element r
+// holds row 4*(l/16)+r, column l%16.
+__device__ __forceinline__ v4f mfma_f8_16x16x128(const v8i& a, const v8i& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// D(16x16, fp32) = A(16x32, bf16) * B(32x16, bf16) + C.
+// Lane l holds row (A) / column (B) l%16 and k = 8*(l/16) .. +7.  Result as above.
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(const v8bf& a, const v8bf& b, const v4f& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposing LDS read of 4 bf16.  Within each group of 16 lanes, with D[m] the
+// four 16-bit values at lane m's address, lane i receives D[4j + i/4][i%4], j=0..3.
+__device__ __forceinline__ v4s lds_read_tr16(const void* lds_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)lds_ptr);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite here).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace dsa

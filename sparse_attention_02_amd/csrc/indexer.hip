@@ -1,0 +1,216 @@
+// Lightning indexer on gfx950 FP8 matrix cores.
+//
+// I[b,t,s] = sum_j w[b,t,j] * ReLU(q_I[b,t,j,:] . k_I[b,s,:]) for s <= pos(t)
+// ("DeepSeek V3.2 and the lightning indexer", section "How the lightning
+// indexer works"; DeepSeek-V3.2 spec sheet, section 2.1: a few indexer heads,
+// weighted sum of ReLU'd dot products, FP8, one key per preceding token).
+//
+// Mapping.  The contraction runs as a GEMM whose rows are (query, head) pairs
+// and whose columns are keys: one v_mfma_f32_16x16x128_f8f6f4 multiplies 16
+// heads of one query by 16 keys over the whole d_I = 128 (shorter d_I is zero
+// padded).  Each lane then owns 4 heads x 1 key of the 16x16 result, applies
+// the ReLU and the head weight in registers and keeps a running partial sum;
+// partial sums over the four lane groups are combined with two butterfly
+// exchanges that also spread the 4 key tiles so that lane l ends with key l of
+// the 64-key stage.  The score row is then written with one coalesced 256-byte
+// store per query.
+//
+// Work split.  A block of 4 waves owns a tile of consecutive query rows of one
+// sequence and walks the keys 0 .. (last position of the tile) in stages:
+//  - prefill (NKL = 1): 4 query groups x 2 queries; every wave reads the same
+//    64-key stage from LDS, so each key byte fetched from L2 feeds 8 queries.
+//  - decode  (NKL = 4): 1 query group; the 4 waves take 4 different 64-key
+//    slices of a 256-key stage (there is nothing to share between queries).
+// Key stages are double-buffered in LDS; the next stage's global loads are in
+// flight while the current one is multiplied.  The causal triangle is skipped
+// at stage granularity; keys past a row's position are computed but not
+// stored.  Blocks are ordered longest-first so the triangle's long rows start
+// early, and long key ranges can be split over several blocks.
+#include "dsa_common.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kQPW = 2;       // queries per wave
+constexpr int kKeysPerWave = 64;
+constexpr int kMaxHG = 4;     // head groups of 16 (H_I <= 64)
+
+template <int NKL>
+__global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
+  constexpr int NQG = 4 / NKL;          // query groups per block
+  constexpr int QT = kQPW * NQG;        // queries per block
+  constexpr int KS = kKeysPerWave * NKL;  // keys per stage
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;              // lane group: k-bytes [32g, 32g+32)
+  const int qgroup = wave % NQG;
+  const int klane = wave / NQG;
+
+  const int bid = blockIdx.x;
+  const int split = bid % a.n_splits;
+  const int rest = bid / a.n_splits;
+  const int b = rest % a.B;
+  const int tile = a.n_qtiles - 1 - rest / a.B;
+
+  const int t_first = tile * QT;
+  const int t_last = min(t_first + QT, a.Lq) - 1;
+  const int kv_end = min(a.Lk, a.q_start + t_last + 1);
+  const int nst_total = (kv_end + KS - 1) / KS;
+  const int st_begin = (int)((long long)nst_total * split / a.n_splits);
+  const int st_end = (int)((long long)nst_total * (split + 1) / a.n_splits);
+  if (st_begin >= st_end) return;
+
+  const int dI = a.dI;
+  const int row_bytes = dI + 16;        // padded LDS row
+  const int stage_bytes = KS * row_bytes;
+  const int nhg = (a.HI + 15) >> 4;
+  const bool g_active = 32 * g < dI;
+
+  // ---- A operands (query heads) and head weights, resident for the whole block
+  v8i qa[kQPW][kMaxHG];
+  float wr[kQPW][kMaxHG][4];
+#pragma unroll
+  for (int q = 0; q < kQPW; ++q) {
+    const int t = t_first + qgroup * kQPW + q;
+#pragma unroll
+    for (int hg = 0; hg < kMaxHG; ++hg) {
+      const int head = 16 * hg + (lane & 15);
+      v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (t < a.Lq && hg < nhg && head < a.HI && g_active) {
+        const uint8_t* src = a.q_idx + (((size_t)b * a.Lq + t) * a.HI + head) * dI + 32 * g;
+        const v4i* s4 = (const v4i*)src;
+        v4i lo = s4[0], hi = s4[1];
+        v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      qa[q][hg] = v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * hg + 4 * g + r;
+        wr[q][hg][r] = (t < a.Lq && h < a.HI) ? a.w[((size_t)b * a.Lq + t) * a.HI + h] : 0.0f;
+      }
+    }
+  }
+
+  // ---- stage loader: KS keys x dI bytes, 16-byte pieces spread over the block
+  const int pieces_per_row = dI >> 4;
+  const int stage_pieces = KS * pieces_per_row;
+  constexpr int kMaxPieces = (KS * 8 + kThreads - 1) / kThreads;  // dI <= 128
+  const uint8_t* kseq = a.k_idx + (size_t)b * a.Lk * dI;
+  v4i pf[kMaxPieces];
+
+  auto load_stage = [&](int st) {
+    const int kbase = st * KS;
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int p = threadIdx.x + j * kThreads;
+      if (p < stage_pieces) {
+        const int key = min(kbase + p / pieces_per_row, a.Lk - 1);
+        pf[j] = *(const v4i*)(kseq + (size_t)key * dI + 16 * (p % pieces_per_row));
+      }
+    }
+  };
+  auto store_stage = [&](int buf) {
+    uint8_t* dst = smem + buf * stage_bytes;
+#pragma unroll
+    for (int j = 0; j < kMaxPieces; ++j) {
+      const int p = threadIdx.x + j * kThreads;
+      if (p < stage_pieces)
+        *(v4i*)(dst + (p / pieces_per_row) * row_bytes + 16 * (p % pieces_per_row)) = pf[j];
+    }
+  };
+
+  load_stage(st_begin);
+  store_stage(0);
+  __syncthreads();
+
+  const bool hi = (lane >> 5) & 1;
+  const bool mid = (lane >> 4) & 1;
+
+  for (int st = st_begin; st < st_end; ++st) {
+    const int buf = (st - st_begin) & 1;
+    if (st + 1 < st_end) load_stage(st + 1);
+
+    const uint8_t* sb = smem + buf * stage_bytes;
+    float part[kQPW][4];
+#pragma unroll
+    for (int q = 0; q < kQPW; ++q)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) part[q][kt] = 0.0f;
+
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key_local = kKeysPerWave * klane + 16 * kt + (lane & 15);
+      v8i kb = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (g_active) {
+        const v4i* s4 = (const v4i*)(sb + key_local * row_bytes + 32 * g);
+        v4i lo = s4[0], hi4 = s4[1];
+        kb = (v8i){lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+#pragma unroll
+      for (int q = 0; q < kQPW; ++q) {
+#pragma unroll
+        for (int hg = 0; hg < kMaxHG; ++hg) {
+          if (hg < nhg) {
+            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            const v4f x = mfma_f8_16x16x128(qa[q][hg], kb, zero);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) part[q][kt] += wr[q][hg][r] * fmaxf(x[r], 0.0f);
+          }
+        }
+      }
+    }
+
+    // ---- head-group reduction + key-tile spread, then the store
+    const int key = st * KS + kKeysPerWave * klane + lane;
+#pragma unroll
+    for (int q = 0; q < kQPW; ++q) {
+      const float s0 = hi ? part[q][0] : part[q][2];
+      const float s1 = hi ? part[q][1] : part[q][3];
+      const float r0 = __shfl_xor(s0, 32);
+      const float r1 = __shfl_xor(s1, 32);
+      const float k0 = (hi ? part[q][2] : part[q][0]) + r0;
+      const float k1 = (hi ? part[q][3] : part[q][1]) + r1;
+      const float snd = mid ? k0 : k1;
+      const float rcv = __shfl_xor(snd, 16);
+      const float fin = (mid ? k1 : k0) + rcv;
+      const int t = t_first + qgroup * kQPW + q;
+      if (t < a.Lq && key <= a.q_start + t && key < a.Lk)
+        a.scores[((size_t)b * a.Lq + t) * a.Lk + key] = fin;
+    }
+
+    if (st + 1 < st_end) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
+  IndexArgs a = args_in;
+  const bool decode = a.Lq < 8;
+  const int QT = decode ? kQPW : kQPW * 4;
+  const int KS = decode ? 4 * kKeysPerWave : kKeysPerWave;
+  a.n_qtiles = (a.Lq + QT - 1) / QT;
+  // Split long key ranges until there are enough blocks to fill the chip.
+  const long long tiles = (long long)a.B * a.n_qtiles;
+  const int max_st = (a.Lk + KS - 1) / KS;
+  int splits = 1;
+  while (tiles * splits < 2048 && splits * 2 <= max_st && splits < 64) splits *= 2;
+  a.n_splits = splits;
+  const size_t smem = 2 * (size_t)KS * (a.dI + 16);
+  const dim3 grid((unsigned)(tiles * splits));
+  if (decode) {
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)index_scores_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
+    return launch_kernel((const void*)index_scores_kernel<4>, grid, dim3(kThreads), smem, stream, a);
+  }
+  return launch_kernel((const void*)index_scores_kernel<1>, grid, dim3(kThreads), smem, stream, a);
+}
+
+}  // namespace dsa

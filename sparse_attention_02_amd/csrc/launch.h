@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (dsa_api.cpp) and the kernels.
+// Arguments here are already validated; the launchers only pick a launch shape.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dsa {
+
+struct IndexArgs {
+  const uint8_t* q_idx;  // [B, Lq, HI, dI] e4m3fn
+  const uint8_t* k_idx;  // [B, Lk, dI]     e4m3fn
+  const float* w;        // [B, Lq, HI]
+  float* scores;         // [B, Lq, Lk]
+  int B, Lq, Lk, q_start, HI, dI;
+  int n_qtiles, n_splits;  // filled by the launcher
+};
+
+struct TopkArgs {
+  const float* scores;  // [B, Lq, Lk]
+  int32_t* indices;     // [B, Lq, k]
+  int B, Lq, Lk, q_start, k;
+};
+
+struct AttnArgs {
+  const uint16_t* q;        // [B, Lq, H, Dqk] bf16
+  const uint16_t* kv;       // [B, Lk, Dqk]    bf16
+  const int32_t* indices;   // [B, Lq, k]
+  float* out;               // [B, Lq, H, Dv]
+  float* lse;               // [B, Lq, H] or null
+  int B, Lq, Lk, H, Dv, Dr, k;
+  float scale_log2;         // softmax_scale * log2(e)
+};
+
+// Launch `kernel(arg)` and return the launch's own status (not the thread's
+// sticky last-error state, which other libraries in the process also write).
+template <typename Arg>
+inline hipError_t launch_kernel(const void* kernel, dim3 grid, dim3 block, size_t smem,
+                                hipStream_t stream, const Arg& arg) {
+  void* args[] = {const_cast<Arg*>(&arg)};
+  return hipLaunchKernel(kernel, grid, block, args, smem, stream);
+}
+
+hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+size_t topk_workspace_bytes(int B, int Lq, int Lk, int k);
+hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,115 @@
+"""C ABI of libdsa.so on the host (no GPU needed).
+
+The library loads, exports every function include/dsa.h declares, and rejects
+bad arguments with the documented status before any HIP call is made (the
+checks below never reach a launch, so they run without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+dsa = pytest.importorskip("sparse_attention_02_amd", reason="libdsa.so not built")
+from sparse_attention_02_amd import DsaError, Problem  # noqa: E402
+
+GOOD = Problem(1, 256, 256, 0, 4, 32, 64, 8, 64, 16, 0.125)
+MLA = Problem(1, 4096, 4096, 0, 64, 128, 2048, 128, 512, 64)
+FAKE = 1 << 20  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
+            "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
+    lib = ctypes.CDLL(dsa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
+
+
+def test_status_strings():
+    for code, text in [(0, "ok"), (-1, "null pointer"), (-3, "unsupported size"),
+                       (-4, "workspace too small"), (-99, "unknown status")]:
+        assert dsa.dsa_status_string(code) == text
+
+
+def _status(fn, *args, **kw):
+    with pytest.raises(DsaError) as e:
+        fn(*args, **kw)
+    return e.value.status, str(e.value)
+
+
+def test_shape_errors():
+    bad = [
+        dict(batch=0), dict(q_len=0), dict(kv_len=0), dict(q_start=-1),
+        dict(q_start=1),  # q_start + q_len > kv_len
+    ]
+    for kw in bad:
+        p = Problem(**{**GOOD.__dict__, **kw})
+        s, msg = _status(dsa.dsa_index_scores, p, FAKE, FAKE, FAKE, FAKE, stream=0)
+        assert s == -2, msg
+    s, _ = _status(dsa.dsa_topk, Problem(**{**GOOD.__dict__, "topk": 0}), FAKE, FAKE, stream=0)
+    assert s == -2
+    for scale in (0.0, -1.0, float("inf"), float("nan")):
+        p = Problem(**{**GOOD.__dict__, "softmax_scale": scale})
+        s, _ = _status(dsa.dsa_sparse_mla_attn, p, FAKE, FAKE, FAKE, FAKE, stream=0)
+        assert s == -2
+
+
+def test_unsupported_sizes():
+    cases = [
+        (dsa.dsa_index_scores, dict(idx_heads=65)),
+        (dsa.dsa_index_scores, dict(idx_dim=48)),
+        (dsa.dsa_index_scores, dict(idx_dim=256)),
+        (dsa.dsa_topk, dict(topk=2049)),
+        (dsa.dsa_sparse_mla_attn, dict(heads=129)),
+        (dsa.dsa_sparse_mla_attn, dict(d_latent=128, d_rope=64)),
+    ]
+    for fn, kw in cases:
+        p = Problem(**{**GOOD.__dict__, **kw})
+        n = {dsa.dsa_index_scores: 4, dsa.dsa_topk: 2, dsa.dsa_sparse_mla_attn: 4}[fn]
+        s, msg = _status(fn, p, *([FAKE] * n), stream=0)
+        assert s == -3, msg
+
+
+def test_null_and_alignment():
+    s, _ = _status(dsa.dsa_index_scores, GOOD, None, FAKE, FAKE, FAKE, stream=0)
+    assert s == -1
+    s, _ = _status(dsa.dsa_sparse_mla_attn, GOOD, FAKE, FAKE, FAKE, None, stream=0)
+    assert s == -1
+    s, msg = _status(dsa.dsa_index_scores, GOOD, FAKE + 8, FAKE, FAKE, FAKE, stream=0)
+    assert s == -5 and "q_idx" in msg
+    s, msg = _status(dsa.dsa_sparse_mla_attn, GOOD, FAKE, FAKE + 2, FAKE, FAKE, stream=0)
+    assert s == -5 and "kv" in msg
+    # a null problem pointer
+    lib = dsa.lib
+    assert lib.dsa_index_scores(None, FAKE, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_workspace_sizes_and_forward_checks():
+    assert dsa.workspace_size(GOOD, dsa.DSA_OP_INDEX_SCORES) == 0
+    assert dsa.workspace_size(GOOD, dsa.DSA_OP_TOPK) == 0
+    ws = dsa.workspace_size(MLA, dsa.DSA_OP_FORWARD)
+    scores = 4096 * 4096 * 4
+    idx = 4096 * 2048 * 4
+    assert ws >= scores + idx and ws % 256 == 0
+    with pytest.raises(DsaError):
+        dsa.workspace_size(Problem(**{**GOOD.__dict__, "batch": 0}), dsa.DSA_OP_FORWARD)
+    s, msg = _status(dsa.dsa_forward, MLA, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                     workspace=FAKE, workspace_bytes=ws - 1, stream=0)
+    assert s == -4, msg
+    s, msg = _status(dsa.dsa_forward, MLA, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                     workspace=FAKE + 16, workspace_bytes=ws, stream=0)
+    assert s == -5, msg
+    s, msg = _status(dsa.dsa_forward, MLA, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                     workspace=None, workspace_bytes=0, stream=0)
+    assert s == -4, msg

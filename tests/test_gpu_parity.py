@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar (from the workload definitions): indexer scores and top-k indices
+bit-exact, sparse-attention output and log-sum-exp within max-abs 1e-2 (fp32).
+The small cases are compared in full; the full-size prefill, decode and
+chunked-prefill workloads are compared on a deterministic row sample (row 0,
+rows k-2..k, the last row, plus random rows) and, on every row, on properties
+of the selection that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs
+import oracle
+from gpu_util import Inputs, check_rows, check_selection_properties, dev, log, run_stages
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_02_amd as m
+    return m
+
+
+def _full_compare(dsa, wl, label):
+    log(f"[{label}] shapes B={wl.batch} Lq={wl.q_len} Lk={wl.kv_len} q_start={wl.q_start} "
+        f"HI={wl.idx_heads} dI={wl.idx_dim} k={wl.topk} H={wl.heads} Dv={wl.d_latent}+{wl.d_rope}")
+    inp = Inputs.make(wl)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
+    sentinel = float("nan")
+    scores, indices, out, lse = run_stages(prob, d, wl, fill_scores=sentinel)
+    # entries after pos(t) are never written
+    s = scores.cpu().numpy()
+    pos = wl.q_start + np.arange(wl.q_len)
+    after = np.arange(wl.kv_len)[None, :] > pos[:, None]
+    assert np.isnan(s[:, after]).all(), "scores written past pos(t)"
+    rows = np.arange(wl.batch * wl.q_len)
+    err, lerr = check_rows(inp, rows, scores, indices, out, lse, ATOL, label)
+    log(f"[{label}] all {len(rows)} rows: scores/indices exact, attn max-abs {err:.3e}, lse {lerr:.3e}")
+    return inp, d, prob, scores, indices, out, lse
+
+
+def test_tiny_full(dsa):
+    wl = dsa_inputs.WORKLOADS["tiny"]
+    inp, d, prob, scores, indices, out, lse = _full_compare(dsa, wl, "tiny")
+    # dsa_forward == the three calls, bit for bit
+    out2 = torch.empty_like(out)
+    lse2 = torch.empty_like(lse)
+    idx2 = torch.empty_like(indices)
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_FORWARD)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    dsa.dsa_forward(prob, d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], out2, lse2, idx2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, indices)
+    assert torch.equal(out2.view(torch.int32), out.view(torch.int32))
+    assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32))
+    # forward without exporting indices
+    out3 = torch.empty_like(out)
+    dsa.dsa_forward(prob, d["q_idx"], d["k_idx"], d["w"], d["q"], d["kv"], out3, None, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out3.view(torch.int32), out.view(torch.int32))
+    # a second run is bit-identical (no races)
+    s2, i2, o2, l2 = run_stages(prob, d, wl, fill_scores=float("nan"))
+    assert torch.equal(s2.view(torch.int32), scores.view(torch.int32))
+    assert torch.equal(i2, indices) and torch.equal(o2.view(torch.int32), out.view(torch.int32))
+
+
+EDGE = {
+    # ragged everything: tails in query tiles, key stages, chunks of 32, heads
+    "ragged": dsa_inputs.Workload("ragged", 11, 2, 77, 300, 223, 5, 64, 50, 20, 64, 16),
+    "single_token": dsa_inputs.Workload("single", 12, 1, 1, 1, 0, 4, 32, 64, 8, 64, 16),
+    "k_above_len": dsa_inputs.Workload("kbig", 13, 1, 40, 40, 0, 4, 32, 64, 8, 64, 16),
+    "wide_indexer": dsa_inputs.Workload("wide", 14, 1, 130, 300, 170, 64, 96, 100, 16, 64, 16),
+    "decode_small": dsa_inputs.Workload("dec", 15, 3, 1, 1000, 999, 64, 128, 128, 16, 64, 16),
+    "few_queries": dsa_inputs.Workload("few", 16, 2, 5, 700, 695, 8, 128, 64, 24, 64, 16),
+    "mla_small": dsa_inputs.Workload("mla", 17, 1, 200, 200, 0, 64, 128, 96, 128, 512, 64),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_shapes_full(dsa, name):
+    _full_compare(dsa, EDGE[name], name)
+
+
+def test_topk_ties_and_signed_zero(dsa):
+    """Heavy ties, exact zeros of both signs, and all-equal rows through dsa_topk."""
+    rng = np.random.default_rng(3)
+    B, Lq, Lk, k = 1, 300, 1500, 96
+    wl = dsa_inputs.Workload("ties", 0, B, Lq, Lk, Lk - Lq, 4, 32, k, 8, 64, 16)
+    s = rng.integers(-3, 4, size=(B, Lq, Lk)).astype(np.float32)
+    s[s == 0] = np.where(rng.random(int((s == 0).sum())) < 0.5, -0.0, 0.0)
+    s[0, :10] = 1.0  # all-equal rows
+    prob = dsa.Problem.from_workload(wl)
+    idx = torch.empty((B, Lq, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(prob, dev(s), idx)
+    torch.cuda.synchronize()
+    pos = (wl.q_start + np.arange(Lq)).astype(np.int32)
+    ref = oracle.topk(s.reshape(Lq, Lk), pos, k)
+    np.testing.assert_array_equal(idx.cpu().numpy().reshape(Lq, k), ref)
+
+
+def test_attention_invalid_entries_and_empty_rows(dsa):
+    wl = dsa_inputs.Workload("inv", 21, 1, 6, 120, 114, 4, 32, 64, 16, 64, 16)
+    inp = Inputs.make(wl)
+    rng = np.random.default_rng(4)
+    idx = np.full((1, 6, 64), -1, np.int32)
+    idx[0, 0, :30] = np.sort(rng.choice(120, 30, replace=False))
+    idx[0, 1, ::2] = rng.choice(120, 32, replace=False)        # unsorted, -1 in between
+    idx[0, 2, :5] = [3, 500, -7, 119, 2 ** 30]                  # out-of-range entries skipped
+    idx[0, 3, 40:] = np.arange(24)                              # only the last chunk valid
+    idx[0, 5, 63] = 7                                           # one valid entry in the tail
+    # row 4 stays all -1: out = 0, lse = -inf
+    prob = dsa.Problem.from_workload(wl)
+    d = inp.device()
+    out = torch.empty((1, 6, 16, 64), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, 6, 16), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], dev(idx), out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.sparse_mla_attn(inp.kv, inp.q, idx[0], np.zeros(6, np.int32), 64,
+                                          wl.softmax_scale)
+    o = out.cpu().numpy()[0]
+    l = lse.cpu().numpy()[0]
+    assert np.abs(o - ref_o).max() <= ATOL
+    assert (o[4] == 0).all() and np.isneginf(l[4]).all()
+    fin = np.isfinite(ref_l)
+    assert np.abs(l[fin] - ref_l[fin]).max() <= ATOL
+
+
+def test_attention_dense_equivalence(dsa):
+    """When every row keeps its whole causal prefix (pos+1 <= k), the sparse path is
+    dense causal MQA attention: compare with torch SDPA in float64 on the CPU."""
+    wl = dsa_inputs.Workload("dense", 22, 1, 64, 64, 0, 4, 32, 64, 32, 512, 64)
+    inp = Inputs.make(wl)
+    prob = dsa.Problem.from_workload(wl)
+    _, indices, out, _ = run_stages(prob, inp.device(), wl)
+    Q = torch.from_numpy(inp.q.view(np.int16).copy()).view(torch.bfloat16).double().permute(1, 0, 2)
+    K = torch.from_numpy(inp.kv[0].view(np.int16).copy()).view(torch.bfloat16).double()
+    K = K.expand(wl.heads, wl.kv_len, wl.d_qk)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        Q, K, K[..., : wl.d_latent], is_causal=True, scale=wl.softmax_scale)
+    err = (out[0].cpu().double() - ref.permute(1, 0, 2)).abs().max().item()
+    assert err <= ATOL, err
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads (sampled rows + properties on every row)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n_random", [("prefill4k", 24), ("prefill32k", 16),
+                                            ("decode", 12), ("chunked", 12)])
+def test_full_size_workloads(dsa, name, n_random):
+    wl = dsa_inputs.WORKLOADS[name]
+    log(f"[{name}] generating inputs")
+    inp = Inputs.make(wl)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
+    log(f"[{name}] running GPU path")
+    scores, indices, out, lse = run_stages(prob, d, wl, fill_scores=float("-inf"))
+    log(f"[{name}] selection properties on all {wl.batch * wl.q_len} rows")
+    check_selection_properties(wl, scores, indices)
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+    rows = dsa_inputs.sample_rows(wl, n_random)
+    log(f"[{name}] oracle on {len(rows)} rows")
+    err, lerr = check_rows(inp, rows, scores, indices, out, lse, ATOL, name)
+    log(f"[{name}] rows {rows.tolist()}: scores/indices exact, attn max-abs {err:.3e}, lse {lerr:.3e}")
+    del scores, indices, out, lse, d
+    torch.cuda.empty_cache()
