@@ -1,0 +1,252 @@
+"""Benchmark of the DeepSeek Sparse Attention hot path on one MI355X.
+
+One step = one pass of the whole path over the L=32K prefill workload (batch 1,
+32768 query tokens, k=2048, FP8 indexer 64 heads x 128, 128 query heads,
+576-wide bf16 latents): dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn,
+launched back to back on one stream (the same launches dsa_forward makes), with
+HIP events between the kernels for per-kernel durations.  Inputs are seeded,
+synthetic and resident in HBM before timing starts.
+
+Prints one JSON line: query tokens/s, per-kernel times and rooflines, and the
+CPU oracle timed on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks.
+PEAK_FP8_TFLOPS = 5000.0    # dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+KERNEL_SOURCES = {
+    "index_scores": "sparse_attention_02_amd/csrc/indexer.hip",
+    "topk": "sparse_attention_02_amd/csrc/topk.hip",
+    "sparse_mla_attn": "sparse_attention_02_amd/csrc/sparse_mla.hip",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle sample")
+    return ap.parse_args()
+
+
+def source_hash(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic(wl):
+    """Algorithmic work per launch (only what the method must do)."""
+    causal = wl.causal_pairs()
+    sel = wl.selected_pairs()
+    rows = wl.batch * wl.q_len
+    return {
+        "index_scores": dict(
+            flop=2.0 * wl.idx_heads * wl.idx_dim * causal,
+            bytes=rows * wl.idx_heads * (wl.idx_dim + 4) + wl.batch * wl.kv_len * wl.idx_dim
+            + 4.0 * causal),
+        "topk": dict(flop=0.0, bytes=4.0 * causal + 4.0 * wl.topk * rows),
+        "sparse_mla_attn": dict(
+            flop=2.0 * wl.heads * (wl.d_qk + wl.d_latent) * sel,
+            bytes=rows * wl.heads * (2 * wl.d_qk + 4 * wl.d_latent + 4) + 4.0 * rows * wl.topk
+            + 2.0 * wl.d_qk * sel),
+    }
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on the
+    current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s: float):
+    """The oracle (as it stands) on an evenly spaced row sample of the workload."""
+    import numpy as np
+
+    import dsa_inputs
+    import oracle
+
+    k_idx = dsa_inputs.k_idx(wl)
+    kv = dsa_inputs.kv(wl)
+
+    def run(n):
+        rows = ((np.arange(n) + 0.5) * (wl.batch * wl.q_len) / n).astype(np.int64)
+        rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+        qi, w, q = dsa_inputs.q_idx(wl, rows), dsa_inputs.w(wl, rows), dsa_inputs.q(wl, rows)
+        t0 = time.perf_counter()
+        oracle.forward(k_idx, qi, w, q, kv, rb, pos, wl.topk, wl.d_latent, wl.softmax_scale)
+        return time.perf_counter() - t0
+
+    threads = oracle.max_threads()
+    pilot_n = max(4, threads)
+    pilot = run(pilot_n)
+    n = int(min(4096, max(pilot_n, pilot_n * target_s / max(pilot, 1e-3))))
+    secs = run(n)
+    return {"value": n / secs, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows evenly spaced over the {wl.q_len}-token sequence "
+                      f"(indexer + top-k + attention per row, {secs:.1f} s wall)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the DSA path here is a single-GPU build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dsa_inputs
+    import sparse_attention_02_amd as dsa
+
+    wl = dsa_inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t_gen = time.perf_counter()
+    q_idx = to_dev(dsa_inputs.q_idx(wl))
+    k_idx = to_dev(dsa_inputs.k_idx(wl))
+    w = to_dev(dsa_inputs.w(wl))
+    kv = to_dev(dsa_inputs.kv(wl))
+    q = to_dev(dsa_inputs.q(wl))
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] inputs for {wl.name} generated and copied in {t_gen:.1f} s", file=sys.stderr,
+          flush=True)
+
+    prob = dsa.Problem.from_workload(wl)
+    B, Lq, Lk = wl.batch, wl.q_len, wl.kv_len
+    scores = torch.empty((B, Lq, Lk), dtype=torch.float32, device=dev)
+    indices = torch.empty((B, Lq, wl.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Lq, wl.heads, wl.d_latent), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Lq, wl.heads), dtype=torch.float32, device=dev)
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    names = ["index_scores", "topk", "sparse_mla_attn"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.dsa_topk(prob, scores, indices, ws, ws_bytes, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    per = {n: [] for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]))
+    step_ms = [ev[0].elapsed_time(ev[3]) for ev in events]
+    ms_per_step = wall * 1e3 / args.steps
+
+    work = algorithmic(wl)
+    kernels = {}
+    for n in names:
+        avg_ms = float(np.mean(per[n]))
+        k = {"avg_ms": avg_ms, "min_ms": float(np.min(per[n])),
+             "algorithmic_flop": work[n]["flop"], "algorithmic_bytes": work[n]["bytes"],
+             "hbm_bytes_per_launch": traffic_for(n)}
+        if work[n]["flop"]:
+            tf = work[n]["flop"] / (avg_ms * 1e-3) / 1e12
+            peak = PEAK_FP8_TFLOPS if n == "index_scores" else PEAK_BF16_TFLOPS
+            k.update(tflops=tf, mfma_peak_tflops=peak, frac_of_mfma_peak=tf / peak)
+        gbs = work[n]["bytes"] / (avg_ms * 1e-3) / 1e9
+        k.update(algorithmic_gbs=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS)
+        kernels[n] = k
+
+    dom = max(names, key=lambda n: kernels[n]["avg_ms"])
+    kd = kernels[dom]
+    if work[dom]["flop"]:
+        roof = {"bound": "mfma", "achieved": kd["tflops"], "peak": kd["mfma_peak_tflops"],
+                "unit": "TFLOP/s", "frac": kd["frac_of_mfma_peak"]}
+    else:
+        roof = {"bound": "hbm", "achieved": kd["algorithmic_gbs"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": kd["frac_of_hbm_peak"]}
+    roof["kernel"] = dom
+    roof["traffic"] = kd["hbm_bytes_per_launch"]
+
+    value = wl.batch * wl.q_len * args.steps / wall
+    result = {
+        "metric": "DSA query tokens/s at L=32K prefill",
+        "value": value,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "event_ms_per_step": float(np.mean(step_ms)),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8/bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len, "kv_len": wl.kv_len,
+                   "q_start": wl.q_start, "topk": wl.topk, "idx_heads": wl.idx_heads,
+                   "idx_dim": wl.idx_dim, "heads": wl.heads, "d_latent": wl.d_latent,
+                   "d_rope": wl.d_rope},
+        "roofline": roof,
+        "indexer_fp8_tflops": kernels["index_scores"]["tflops"],
+        "indexer_frac_of_fp8_peak": kernels["index_scores"]["frac_of_mfma_peak"],
+        "kernels": kernels,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del scores, indices, out, lse, q, q_idx
+        torch.cuda.empty_cache()
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
