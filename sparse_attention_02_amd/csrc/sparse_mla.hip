@@ -10,19 +10,29 @@
 // non-contiguous gather affordable (inference-research record on DSA: sparse
 // attention loses to dense unless selection is group-shared).
 //
-// Mapping.  One block per query row; wave w owns heads [16w, 16w+16).  The
-// selected latent rows are gathered 32 at a time straight into LDS with
-// global_load_lds (no register staging), double-buffered so the next chunk's
-// gather overlaps this chunk's math.  Every wave reads the same chunk:
-//   S^T[key, head] = K_chunk . Q^T   bf16 MFMA 16x16x32, Q^T held in registers
-//   online softmax in fp32 (exp2 domain), P rounded to bf16
-//   O^T[d, head]  += V^T . P^T       bf16 MFMA 16x16x32
-// The MFMA result layout of S^T leaves each lane with one head and 8 keys,
-// which is exactly a B operand of the value product once the 32 keys of the
-// chunk are taken in the order (4g..4g+3, 16+4g..16+4g+3) for lane group g;
-// the matching V^T operand comes from row-major LDS through the transposing
-// ds_read_b64_tr_b16.  So P never leaves registers and the latent chunk is
-// stored once, row-major, for both products.
+// Mapping (one block of NW waves per query row):
+//  * Gather: the selected latent rows are copied 32 at a time straight into
+//    LDS with global_load_lds (no register staging), three chunks in flight.
+//    Rows are stored with their 16-byte pieces XOR-swizzled by (row & 7) so the
+//    operand reads below are free of LDS bank conflicts.
+//  * Scores: wave w owns 16*HTQ heads.  S^T[key, head] = K . Q^T on bf16 MFMA
+//    16x16x32 with Q^T resident in registers.
+//  * Softmax: fp32 in the exp2 domain with a lazily moved running maximum (the
+//    accumulators are only rescaled when a head's maximum grows by more than
+//    2^8, so probabilities stay <= 256).  P is rounded to bf16 and exchanged
+//    through LDS together with the per-head rescale factors.
+//  * Values: wave w owns output columns [DV/NW * w, DV/NW * (w+1)) for all 128
+//    heads: O^T[d, head] += V^T . P^T on bf16 MFMA 16x16x32.  V^T comes from the
+//    row-major latent chunk through the transposing ds_read_b64_tr_b16 and is
+//    reused by all eight 16-head tiles, so the slower transposing reads are
+//    issued once per wave and d-tile, not once per head tile.
+// Per SIMD, Q (128 heads) and the fp32 output accumulators (128 x 512) take
+// about 400 of the 512 registers whatever the split; NW = 8 runs two waves per
+// SIMD so one wave's softmax overlaps the other's matrix work.
+// The MFMA result layout of S^T leaves a lane with one head and the 8 keys
+// {4g..4g+3, 16+4g..16+4g+3} (g = lane/16); those 8 values are written as one
+// 16-byte row segment of P, and the V^T operand of lane group g reads exactly
+// those 8 latent rows, so both operands agree on the key order.
 #include "dsa_common.h"
 #include "launch.h"
 
@@ -30,202 +40,339 @@ namespace dsa {
 
 namespace {
 
-constexpr int kChunk = 32;
+constexpr int kChunk = 32;     // keys per chunk
+constexpr int kStages = 3;     // latent chunks in flight
+constexpr int kHeadTiles = 8;  // 128 heads / 16
+constexpr int kPRow = 64;      // bytes of one head's P row (32 bf16)
+constexpr float kLazyMax = 8.0f;
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NW>
 struct AttnShape {
   static constexpr int DQKP = (DQK + 31) / 32 * 32;  // score width padded to K=32 steps
   static constexpr int KST = DQKP / 32;
-  static constexpr int DT = DV / 16;
+  static constexpr int HTQ = 128 / 16 / NW;         // 16-head score tiles per wave
+  static constexpr int DTW = DV / 16 / NW;          // value d-tiles per wave
   static constexpr int RS = DQKP * 2;               // LDS bytes per latent row
   static constexpr int PPR = RS / 16;               // 16-byte pieces per LDS row
   static constexpr int RPR = DQK * 2 / 16;          // pieces present in the cache row
   static constexpr int CHUNK_BYTES = kChunk * RS;
   static constexpr int DMA_BLOCKS = CHUNK_BYTES / 1024;  // 64 lanes x 16 bytes
+  static constexpr bool SWZ = PPR % 8 == 0;
+  static constexpr int DMA_LO = DMA_BLOCKS / NW;    // DMA blocks of waves >= DMA_BLOCKS % NW
+  static constexpr int DMA_HI_WAVES = DMA_BLOCKS % NW;
+  static constexpr int P_BYTES = 128 * kPRow;
   static_assert(CHUNK_BYTES % 1024 == 0, "chunk must be whole 1 KiB DMA blocks");
-  static_assert(DQK % 8 == 0 && DV % 16 == 0 && DV <= DQK, "unsupported latent shape");
+  static_assert(HTQ >= 1 && HTQ * 16 * NW == 128, "score heads must tile 128");
+  static_assert(DQK % 8 == 0 && DTW >= 1 && DTW * 16 * NW == DV && DV <= DQK, "unsupported latent shape");
 };
 
-template <int DQK, int DV>
-__global__ __launch_bounds__(512) void sparse_mla_kernel(AttnArgs a) {
-  using S = AttnShape<DQK, DV>;
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16-byte global -> LDS copy of lane i from (base + offset_i) to (m0 + 16 i).
+// Issued through inline assembly so that the compiler does not insert a
+// conservative wait for it before every later LDS read; completion is tracked
+// with explicit vmcnt waits.  `base` is wave-uniform (SGPR pair).
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* base, uint32_t offset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(offset), "s"(base) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int DQK, int DV, int NW>
+__global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
+  using S = AttnShape<DQK, DV, NW>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* bufs = smem;                                           // [2][CHUNK_BYTES]
-  int32_t* sidx = (int32_t*)(smem + 2 * S::CHUNK_BYTES);          // [nch * kChunk]
+  uint8_t* kvb = smem;                                        // [kStages][CHUNK_BYTES]
+  uint8_t* pbuf = smem + kStages * S::CHUNK_BYTES;            // [2][128 heads][kPRow]
+  float* alpha_s = (float*)(pbuf + 2 * S::P_BYTES);           // [2][128]
+  float* lsum_s = alpha_s + 2 * 128;                          // [128]
+  int32_t* sidx = (int32_t*)(lsum_s + 128);                   // [nch * kChunk]
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = blockDim.x >> 6;
   const int g = lane >> 4;
   const int li = lane & 15;
   const int row = blockIdx.x;
   const int b = row / a.Lq;
   const int nch = (a.k + kChunk - 1) / kChunk;
 
-  // ---- selected indices -> LDS; chunk validity mask (k <= 2048 -> nch <= 64)
+  // ---- selected indices -> LDS (entries outside [0, Lk) become -1)
   const int32_t* idx_row = a.indices + (size_t)row * a.k;
   for (int i = threadIdx.x; i < nch * kChunk; i += blockDim.x) {
-    int v = i < a.k ? idx_row[i] : -1;
+    const int v = i < a.k ? idx_row[i] : -1;
     sidx[i] = (v >= 0 && v < a.Lk) ? v : -1;
   }
   __syncthreads();
-  uint64_t chunk_mask = 0;
+  uint64_t chunk_mask;
   {
     bool any = false;
-    if (lane < nch) {
+    if (lane < nch)
       for (int j = 0; j < kChunk; ++j) any |= sidx[lane * kChunk + j] >= 0;
-    }
     chunk_mask = __ballot(any);
   }
 
-  // ---- Q^T fragments of this wave's 16 heads (B operand of the score product)
-  const int head = 16 * wave + li;
-  const bool head_ok = head < a.H;
-  v8bf qf[S::KST];
-  {
-    const uint16_t* qrow = a.q + ((size_t)row * a.H + (head_ok ? head : 0)) * DQK;
+  // ---- Q^T fragments of this wave's score heads (B operand)
+  v8bf qf[S::HTQ][S::KST];
+#pragma unroll
+  for (int ht = 0; ht < S::HTQ; ++ht) {
+    const int head = 16 * (S::HTQ * wave + ht) + li;
+    const bool ok = head < a.H;
+    const uint16_t* qrow = a.q + ((size_t)row * a.H + (ok ? head : 0)) * DQK;
 #pragma unroll
     for (int ks = 0; ks < S::KST; ++ks) {
       const int d0 = 32 * ks + 8 * g;
       v4i v = {0, 0, 0, 0};
-      if (head_ok && d0 + 8 <= DQK) v = *(const v4i*)(qrow + d0);
-      qf[ks] = __builtin_bit_cast(v8bf, v);
+      if (d0 + 8 <= DQK) v = *(const v4i*)(qrow + (d0 + 8 <= DQK ? d0 : 0));  // compile-time for DQK % 32 == 0
+      if (!ok) v = (v4i){0, 0, 0, 0};
+      qf[ht][ks] = __builtin_bit_cast(v8bf, v);
     }
   }
 
+  // ---- gather of one chunk: this wave's 1 KiB DMA blocks
   const uint8_t* kv_seq = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK);
-  auto gather = [&](int c, int buf) {
-    uint8_t* dst = bufs + buf * S::CHUNK_BYTES;
-    for (int j = wave; j < S::DMA_BLOCKS; j += nwaves) {
-      const int p = 64 * j + lane;
-      const int r = p / S::PPR, col = p % S::PPR;
-      const int idx = sidx[c * kChunk + r];
-      const int src_row = idx >= 0 ? idx : 0;
-      const int src_col = col < S::RPR ? col : col - S::RPR;  // pad pieces meet zero q
-      const uint8_t* src = kv_seq + (size_t)src_row * (DQK * 2) + 16 * src_col;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (__attribute__((address_space(3))) void*)(dst + 1024 * j),
-                                       16, 0, 0);
+  auto issue = [&](int c, int buf) {
+    uint8_t* dst = kvb + buf * S::CHUNK_BYTES;
+#pragma unroll
+    for (int j0 = 0; j0 < (S::DMA_BLOCKS + NW - 1) / NW; ++j0) {
+      const int j = j0 * NW + wave;
+      if (j < S::DMA_BLOCKS) {
+        const int p = 64 * j + lane;
+        const int r = p / S::PPR, pp = p % S::PPR;
+        const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
+        const int idx = sidx[c * kChunk + r];
+        const int src_row = idx >= 0 ? idx : 0;
+        const int src_col = lp < S::RPR ? lp : lp - S::RPR;  // pad pieces meet zero q
+        dma16(__builtin_amdgcn_readfirstlane(lds_offset(dst + 1024 * j)), kv_seq,
+              (uint32_t)src_row * (DQK * 2) + 16 * src_col);
+      }
     }
   };
 
-  v4f acc[S::DT];
+  // physical byte offset of logical 16-byte piece `lp` in LDS row `r`
+  auto piece = [](int r, int lp) { return 16 * (S::SWZ ? (lp ^ (r & 7)) : lp); };
+
+  v4f acc[kHeadTiles][S::DTW];
 #pragma unroll
-  for (int dt = 0; dt < S::DT; ++dt) acc[dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = -INFINITY;
-  float l_part = 0.0f;
-
-  uint64_t pending = chunk_mask;
-  int cur = pending ? __builtin_ctzll(pending) : -1;
-  if (cur >= 0) {
-    pending &= pending - 1;
-    gather(cur, 0);
+  for (int ht = 0; ht < kHeadTiles; ++ht)
+#pragma unroll
+    for (int dt = 0; dt < S::DTW; ++dt) acc[ht][dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  float m_use[S::HTQ], l_part[S::HTQ];
+#pragma unroll
+  for (int ht = 0; ht < S::HTQ; ++ht) {
+    m_use[ht] = -INFINITY;
+    l_part[ht] = 0.0f;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
 
-  int buf = 0;
-  while (cur >= 0) {
-    const int nxt = pending ? __builtin_ctzll(pending) : -1;
-    if (nxt >= 0) {
-      pending &= pending - 1;
-      gather(nxt, buf ^ 1);
+  uint64_t to_issue = chunk_mask;
+  uint64_t to_compute = chunk_mask;
+  const int total = __builtin_popcountll(chunk_mask);
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) {
+    if (to_issue) {
+      issue(__builtin_ctzll(to_issue), s);
+      to_issue &= to_issue - 1;
     }
-    const uint8_t* kb = bufs + buf * S::CHUNK_BYTES;
+  }
 
-    // ---- S^T = K_chunk . Q^T  (two 16-key tiles)
-    v4f s[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  // Per-lane LDS byte offsets of the operand reads.  With the swizzle, logical
+  // piece lp of row r sits at piece lp ^ (r & 7): 8*(lp>>3) + ((lp&7) ^ (r&7)).
+  //  K rows 16kt + li (row & 7 == li & 7); logical piece 4ks + g, so piece
+  //  8*(ks>>1) + ((4*(ks&1) + g) ^ (li&7)): a per-lane base per ks parity plus
+  //  a compile-time 128-byte step.
+  int k_off[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) k_off[par] = li * S::RS + piece(li, 4 * par + g);
+  //  V^T rows 4g + li/4 (k-slots 8g..8g+3) and 16 + 4g + li/4 (8g+4..8g+7),
+  //  both with row & 7 == (4g + li/4) & 7; logical piece 2*dtg + (li&3)/2 of
+  //  d-tile dtg, plus 8*(li&1) bytes inside the piece.
+  const int r_v0 = 4 * g + (li >> 2);
+  const int v_base = r_v0 * S::RS + 8 * (li & 1);
+  const int v_sel = (li & 3) >> 1;
+  //  P row of head 16ht + li, piece g ^ ((head >> 2) & 3) == g ^ ((li >> 2) & 3)
+  const int p_off = li * kPRow + 16 * (g ^ ((li >> 2) & 3));
+
+  for (int it = 0; to_compute; ++it) {
+    const int c = __builtin_ctzll(to_compute);
+    to_compute &= to_compute - 1;
+    const int buf = it % kStages;
+    const uint8_t* kb = kvb + buf * S::CHUNK_BYTES;
+    const int pslot = it & 1;
+
+    // wait for this chunk's gather: at most one later chunk is in flight here
+    if (it + 1 < total) {
+      if (wave < S::DMA_HI_WAVES) wait_vmcnt<S::DMA_LO + 1>();
+      else wait_vmcnt<S::DMA_LO>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __syncthreads();
+
+    // ---- S^T = K_chunk . Q^T for 2 key tiles x HTQ head tiles
+    v4f s[S::HTQ][2];
+#pragma unroll
+    for (int ht = 0; ht < S::HTQ; ++ht)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[ht][kt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    // K fragments are prefetched two K-steps ahead; the scheduling fences keep
+    // the compiler from hoisting the whole chunk's loads (register pressure).
+    constexpr int kPre = 2;
+    v8bf kf[kPre + 1][2];
+    auto load_k = [&](int ks, v8bf* dst) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        dst[kt] = __builtin_bit_cast(
+            v8bf, *(const v4i*)(kb + k_off[ks & 1] + 16 * kt * S::RS + 128 * (ks >> 1)));
+    };
+#pragma unroll
+    for (int ks = 0; ks < kPre && ks < S::KST; ++ks) load_k(ks, kf[ks]);
 #pragma unroll
     for (int ks = 0; ks < S::KST; ++ks) {
+      if (ks + kPre < S::KST) load_k(ks + kPre, kf[(ks + kPre) % (kPre + 1)]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const v4i raw = *(const v4i*)(kb + (16 * kt + li) * S::RS + (32 * ks + 8 * g) * 2);
-        s[kt] = mfma_bf16_16x16x32(__builtin_bit_cast(v8bf, raw), qf[ks], s[kt]);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ht = 0; ht < S::HTQ; ++ht)
+          s[ht][kt] = mfma_bf16_16x16x32(kf[ks % (kPre + 1)][kt], qf[ht][ks], s[ht][kt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- softmax for this lane's heads over its 8 keys; P and alpha -> LDS
+    const v4i id0 = *(const v4i*)(sidx + c * kChunk + 4 * g);
+    const v4i id1 = *(const v4i*)(sidx + c * kChunk + 16 + 4 * g);
+#pragma unroll
+    for (int ht = 0; ht < S::HTQ; ++ht) {
+      float z[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        z[r] = id0[r] >= 0 ? s[ht][0][r] * a.scale_log2 : -INFINITY;
+        z[4 + r] = id1[r] >= 0 ? s[ht][1][r] * a.scale_log2 : -INFINITY;
       }
-    }
-
-    // ---- online softmax for this lane's head over its 8 keys
-    const v4i id0 = *(const v4i*)(sidx + cur * kChunk + 4 * g);
-    const v4i id1 = *(const v4i*)(sidx + cur * kChunk + 16 + 4 * g);
-    float z[8];
+      float mloc = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
+                         fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      float al = 1.0f;
+      if (mloc > m_use[ht] + kLazyMax) {
+        al = fast_exp2(m_use[ht] - mloc);
+        m_use[ht] = mloc;
+      }
+      uint32_t pk[4];
+      float psum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      z[r] = id0[r] >= 0 ? s[0][r] * a.scale_log2 : -INFINITY;
-      z[4 + r] = id1[r] >= 0 ? s[1][r] * a.scale_log2 : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = float_to_bf16_bits(fast_exp2(z[2 * i] - m_use[ht]));
+        const uint32_t hi = float_to_bf16_bits(fast_exp2(z[2 * i + 1] - m_use[ht]));
+        psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);
+        pk[i] = lo | (hi << 16);
+      }
+      l_part[ht] = l_part[ht] * al + psum;
+      const int head = 16 * (S::HTQ * wave + ht) + li;
+      *(v4i*)(pbuf + pslot * S::P_BYTES + head * kPRow + 16 * (g ^ ((head >> 2) & 3))) =
+          (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+      if (g == 0) alpha_s[pslot * 128 + head] = al;
     }
-    float mloc = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mloc = fmaxf(mloc, z[i]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    uint32_t pk[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = float_to_bf16_bits(fast_exp2(z[2 * i] - m_new));
-      const uint32_t hi = float_to_bf16_bits(fast_exp2(z[2 * i + 1] - m_new));
-      psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);
-      pk[i] = lo | (hi << 16);
-    }
-    l_part = l_part * alpha + psum;
-    const v8bf pb = __builtin_bit_cast(v8bf, (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
-
-    // ---- O^T = alpha * O^T + V^T . P^T
-    const uint8_t* vrow0 = kb + (4 * g + (li >> 2)) * S::RS + 4 * (li & 3) * 2;
-    const uint8_t* vrow1 = vrow0 + 16 * S::RS;
-#pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) {
-      const v4s lo = lds_read_tr16(vrow0 + 32 * dt);
-      const v4s hi = lds_read_tr16(vrow1 + 32 * dt);
-      const v8bf va = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-      acc[dt] = mfma_bf16_16x16x32(va, pb, acc[dt] * alpha);
-    }
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    cur = nxt;
-    buf ^= 1;
+
+    // the chunk before this one is done everywhere: reuse its buffer for the next gather
+    if (to_issue) {
+      issue(__builtin_ctzll(to_issue), (it + kStages - 1) % kStages);
+      to_issue &= to_issue - 1;
+    }
+
+    // ---- O^T = alpha * O^T + V^T . P^T for this wave's d-range, all 128 heads
+    float al8[kHeadTiles];
+    bool rescale = false;
+#pragma unroll
+    for (int ht = 0; ht < kHeadTiles; ++ht) {
+      al8[ht] = alpha_s[pslot * 128 + 16 * ht + li];
+      rescale |= al8[ht] != 1.0f;
+    }
+    if (__ballot(rescale)) {
+#pragma unroll
+      for (int ht = 0; ht < kHeadTiles; ++ht)
+#pragma unroll
+        for (int dt = 0; dt < S::DTW; ++dt) acc[ht][dt] *= al8[ht];
+    }
+    // V^T fragments of this wave's d-tiles, then one P fragment per head tile
+    v8bf va[S::DTW];
+#pragma unroll
+    for (int dt = 0; dt < S::DTW; ++dt) {
+      const int voff = v_base + piece(r_v0, 2 * (wave * S::DTW + dt) + v_sel);
+      const v4s lo = lds_read_tr16(kb + voff);
+      const v4s hi = lds_read_tr16(kb + voff + 16 * S::RS);
+      va[dt] = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
+    const uint8_t* pb = pbuf + pslot * S::P_BYTES + p_off;
+    auto load_p = [&](int ht) { return __builtin_bit_cast(v8bf, *(const v4i*)(pb + 16 * kPRow * ht)); };
+    v8bf pf[2];
+    pf[0] = load_p(0);
+#pragma unroll
+    for (int ht = 0; ht < kHeadTiles; ++ht) {
+      if (ht + 1 < kHeadTiles) pf[(ht + 1) & 1] = load_p(ht + 1);
+#pragma unroll
+      for (int dt = 0; dt < S::DTW; ++dt) acc[ht][dt] = mfma_bf16_16x16x32(va[dt], pf[ht & 1], acc[ht][dt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
-  // ---- normalise and store
-  float l_tot = l_part + __shfl_xor(l_part, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (head_ok) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    float* orow = a.out + ((size_t)row * a.H + head) * DV;
+  // ---- row sums of the score heads -> LDS; lse
 #pragma unroll
-    for (int dt = 0; dt < S::DT; ++dt) {
-      const v4f o = acc[dt] * inv;
-      *(v4f*)(orow + 16 * dt + 4 * g) = o;
+  for (int ht = 0; ht < S::HTQ; ++ht) {
+    float l = l_part[ht] + __shfl_xor(l_part[ht], 16);
+    l += __shfl_xor(l, 32);
+    const int head = 16 * (S::HTQ * wave + ht) + li;
+    if (g == 0) {
+      lsum_s[head] = l;
+      if (a.lse && head < a.H)
+        a.lse[(size_t)row * a.H + head] =
+            l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
     }
-    if (a.lse && g == 0)
-      a.lse[(size_t)row * a.H + head] =
-          l_tot > 0.0f ? (m_run + fast_log2(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  }
+  __syncthreads();
+
+  // ---- normalise and store this wave's columns of every head
+#pragma unroll
+  for (int ht = 0; ht < kHeadTiles; ++ht) {
+    const int head = 16 * ht + li;
+    if (head < a.H) {
+      const float l = lsum_s[head];
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      float* orow = a.out + ((size_t)row * a.H + head) * DV;
+#pragma unroll
+      for (int dt = 0; dt < S::DTW; ++dt) {
+        const int d0 = 16 * (wave * S::DTW + dt) + 4 * g;
+        *(v4f*)(orow + d0) = acc[ht][dt] * inv;
+      }
+    }
   }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NW>
 hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
-  using S = AttnShape<DQK, DV>;
+  using S = AttnShape<DQK, DV, NW>;
   const int nch = (a.k + kChunk - 1) / kChunk;
-  const size_t smem = 2 * (size_t)S::CHUNK_BYTES + (size_t)nch * kChunk * sizeof(int32_t);
-  const int nwaves = (a.H + 15) / 16;
+  const size_t smem = (size_t)kStages * S::CHUNK_BYTES + 2 * (size_t)S::P_BYTES +
+                      3 * 128 * sizeof(float) + (size_t)nch * kChunk * sizeof(int32_t);
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)sparse_mla_kernel<DQK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (const void*)sparse_mla_kernel<DQK, DV, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
       160 * 1024);
   if (attr != hipSuccess) return attr;
-  return launch_kernel((const void*)sparse_mla_kernel<DQK, DV>,
-                       dim3((unsigned)((long long)a.B * a.Lq)), dim3(64 * nwaves), smem, stream, a);
+  return launch_kernel((const void*)sparse_mla_kernel<DQK, DV, NW>,
+                       dim3((unsigned)((long long)a.B * a.Lq)), dim3(64 * NW), smem, stream, a);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream) {
-  if (a.Dv == 512 && a.Dr == 64) return launch_shape<576, 512>(a, stream);
-  if (a.Dv == 64 && a.Dr == 16) return launch_shape<80, 64>(a, stream);
+  if (a.Dv == 512 && a.Dr == 64) return launch_shape<576, 512, 8>(a, stream);
+  if (a.Dv == 64 && a.Dr == 16) return launch_shape<80, 64, 4>(a, stream);
   return hipErrorInvalidValue;
 }
 
