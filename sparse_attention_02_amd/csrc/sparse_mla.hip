@@ -91,7 +91,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* kvb = smem;                                        // [kStages][CHUNK_BYTES]
   uint8_t* pbuf = smem + kStages * S::CHUNK_BYTES;            // [2][128 heads][kPRow]
-  float* alpha_s = (float*)(pbuf + 2 * S::P_BYTES);           // [2][128]
+  float* alpha_s = (float*)(pbuf + 2 * S::P_BYTES);           // [2][16 lanes][8 head tiles]
   float* lsum_s = alpha_s + 2 * 128;                          // [128]
   int32_t* sidx = (int32_t*)(lsum_s + 128);                   // [nch * kChunk]
 
@@ -110,12 +110,17 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     sidx[i] = (v >= 0 && v < a.Lk) ? v : -1;
   }
   __syncthreads();
-  uint64_t chunk_mask;
+  uint64_t chunk_mask, full_mask;  // chunks with some / with only valid entries
   {
-    bool any = false;
+    bool any = false, all = lane < nch;
     if (lane < nch)
-      for (int j = 0; j < kChunk; ++j) any |= sidx[lane * kChunk + j] >= 0;
+      for (int j = 0; j < kChunk; ++j) {
+        const bool v = sidx[lane * kChunk + j] >= 0;
+        any |= v;
+        all &= v;
+      }
     chunk_mask = __ballot(any);
+    full_mask = __ballot(all);
   }
 
   // ---- Q^T fragments of this wave's score heads (B operand)
@@ -244,8 +249,12 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     }
 
     // ---- softmax for this lane's heads over its 8 keys; P and alpha -> LDS
-    const v4i id0 = *(const v4i*)(sidx + c * kChunk + 4 * g);
-    const v4i id1 = *(const v4i*)(sidx + c * kChunk + 16 + 4 * g);
+    const bool full = (full_mask >> c) & 1;
+    v4i id0 = {0, 0, 0, 0}, id1 = {0, 0, 0, 0};
+    if (!full) {
+      id0 = *(const v4i*)(sidx + c * kChunk + 4 * g);
+      id1 = *(const v4i*)(sidx + c * kChunk + 16 + 4 * g);
+    }
 #pragma unroll
     for (int ht = 0; ht < S::HTQ; ++ht) {
       float z[8];
@@ -256,8 +265,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       }
       float mloc = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
                          fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+      mloc = max_xor32(max_xor16(mloc));
       float al = 1.0f;
       if (mloc > m_use[ht] + kLazyMax) {
         al = fast_exp2(m_use[ht] - mloc);
@@ -267,16 +275,16 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = float_to_bf16_bits(fast_exp2(z[2 * i] - m_use[ht]));
-        const uint32_t hi = float_to_bf16_bits(fast_exp2(z[2 * i + 1] - m_use[ht]));
-        psum += bf16_bits_to_float(lo) + bf16_bits_to_float(hi);
-        pk[i] = lo | (hi << 16);
+        const float p0 = fast_exp2(z[2 * i] - m_use[ht]);
+        const float p1 = fast_exp2(z[2 * i + 1] - m_use[ht]);
+        psum += p0 + p1;
+        pk[i] = pack_bf16x2(p0, p1);
       }
       l_part[ht] = l_part[ht] * al + psum;
       const int head = 16 * (S::HTQ * wave + ht) + li;
       *(v4i*)(pbuf + pslot * S::P_BYTES + head * kPRow + 16 * (g ^ ((head >> 2) & 3))) =
           (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-      if (g == 0) alpha_s[pslot * 128 + head] = al;
+      if (g == 0) alpha_s[pslot * 128 + li * kHeadTiles + (head >> 4)] = al;
     }
     __syncthreads();
 
@@ -288,12 +296,18 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
 
     // ---- O^T = alpha * O^T + V^T . P^T for this wave's d-range, all 128 heads
     float al8[kHeadTiles];
+    {
+      const v4f a0 = *(const v4f*)(alpha_s + pslot * 128 + li * kHeadTiles);
+      const v4f a1 = *(const v4f*)(alpha_s + pslot * 128 + li * kHeadTiles + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        al8[i] = a0[i];
+        al8[4 + i] = a1[i];
+      }
+    }
     bool rescale = false;
 #pragma unroll
-    for (int ht = 0; ht < kHeadTiles; ++ht) {
-      al8[ht] = alpha_s[pslot * 128 + 16 * ht + li];
-      rescale |= al8[ht] != 1.0f;
-    }
+    for (int ht = 0; ht < kHeadTiles; ++ht) rescale |= al8[ht] != 1.0f;
     if (__ballot(rescale)) {
 #pragma unroll
       for (int ht = 0; ht < kHeadTiles; ++ht)

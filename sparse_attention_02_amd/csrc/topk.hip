@@ -161,6 +161,104 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   }
 }
 
+// Register-resident variant for rows of at most EPT * kThreads candidates:
+// thread t holds the keys of the contiguous candidates [EPT*t, EPT*t + EPT), so
+// the digit passes touch LDS only for the histogram and the ordered compaction
+// needs a single block-wide scan.  LDS use is ~8 KiB, so several rows run per
+// CU.  VEC loads the segment with 16-byte loads (row stride a multiple of 4).
+template <int EPT, bool VEC>
+__global__ __launch_bounds__(kThreads) void topk_reg_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t scan_sh[kWaves + 1];
+  __shared__ uint32_t ctrl[4];
+
+  const int row = blockIdx.x;
+  const int t = row % a.Lq;
+  const int pos = a.q_start + t;
+  const int n = min(pos + 1, a.Lk);
+  int32_t* out = a.indices + (size_t)row * a.k;
+  if (n <= a.k) {
+    for (int i = threadIdx.x; i < a.k; i += kThreads) out[i] = i < n ? i : -1;
+    return;
+  }
+  const float* srow = a.scores + (size_t)row * a.Lk;
+  const int base = EPT * threadIdx.x;
+  const int cnt = max(0, min(EPT, n - base));  // valid candidates of this thread
+
+  uint32_t key[EPT];
+  if (VEC && cnt == EPT) {
+#pragma unroll
+    for (int j = 0; j < EPT; j += 4) {
+      const v4f v = *(const v4f*)(srow + base + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[j + e] = order_key(v[e]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) key[j] = j < cnt ? order_key(srow[base + j]) : 0u;
+  }
+
+  uint32_t prefix = 0, mask = 0;
+  uint32_t need = (uint32_t)a.k;
+  bool all_ge = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (j < cnt && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
+    __syncthreads();
+    const int b0 = kBins - 1 - 2 * (int)threadIdx.x, b1 = b0 - 1;
+    const uint32_t h0 = hist[b0], h1 = hist[b1];
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan(h0 + h1, scan_sh, total);
+    const uint32_t excl = incl - h0 - h1;
+    if (excl < need && need <= excl + h0) { ctrl[0] = (uint32_t)b0; ctrl[1] = excl; }
+    if (excl + h0 < need && need <= incl) { ctrl[0] = (uint32_t)b1; ctrl[1] = excl + h0; }
+    __syncthreads();
+    const uint32_t d = ctrl[0];
+    need -= ctrl[1];
+    prefix |= d << shift;
+    mask |= dmask << shift;
+    const uint32_t bin_count = hist[d];
+    __syncthreads();
+    if (bin_count == need) { all_ge = true; break; }
+  }
+
+  // ---- ordered compaction: one scan of per-thread (greater, equal) counts
+  const uint32_t T = prefix;
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (j < cnt) {
+      gt += all_ge ? key[j] >= T : key[j] > T;
+      eq += !all_ge && key[j] == T;
+    }
+  }
+  uint32_t total;
+  const uint32_t packed = gt | (eq << 16);
+  const uint32_t excl = block_inclusive_scan(packed, scan_sh, total) - packed;
+  uint32_t gt_before = excl & 0xFFFFu, eq_before = excl >> 16;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    if (j < cnt) {
+      const bool is_gt = all_ge ? key[j] >= T : key[j] > T;
+      const bool is_eq = !all_ge && key[j] == T;
+      if (is_gt) {
+        const uint32_t o = gt_before + min(eq_before, need);
+        if (o < (uint32_t)a.k) out[o] = base + j;
+        ++gt_before;
+      } else if (is_eq) {
+        if (eq_before < need && gt_before + eq_before < (uint32_t)a.k) out[gt_before + eq_before] = base + j;
+        ++eq_before;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int, int, int, int) { return 0; }
@@ -169,6 +267,11 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((long long)a.B * a.Lq));
   const int max_n = min(a.q_start + a.Lq, a.Lk);
   const size_t base = (size_t)(kBins + kWaves + 1 + 4) * sizeof(uint32_t);
+  if (max_n <= 32 * kThreads) {
+    if (a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0)
+      return launch_kernel((const void*)topk_reg_kernel<32, true>, grid, dim3(kThreads), 0, stream, a);
+    return launch_kernel((const void*)topk_reg_kernel<32, false>, grid, dim3(kThreads), 0, stream, a);
+  }
   if (max_n <= kCacheMax) {
     static const hipError_t attr = hipFuncSetAttribute(
         (const void*)topk_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
