@@ -59,6 +59,33 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* s
   return v + add;
 }
 
+template <int NT>
+__device__ __forceinline__ uint32_t block_inclusive_scan_n(uint32_t v, uint32_t* sh, uint32_t& total) {
+  constexpr int NWV = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t x = lane < NWV ? sh[lane] : 0u;
+#pragma unroll
+    for (int o = 1; o < NWV; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane < NWV) sh[lane] = x;
+  }
+  __syncthreads();
+  const uint32_t add = wave > 0 ? sh[wave - 1] : 0u;
+  total = sh[NWV - 1];
+  __syncthreads();
+  return v + add;
+}
+
 template <bool CACHED>
 __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
@@ -166,10 +193,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
 // the digit passes touch LDS only for the histogram and the ordered compaction
 // needs a single block-wide scan.  LDS use is ~8 KiB, so several rows run per
 // CU.  VEC loads the segment with 16-byte loads (row stride a multiple of 4).
-template <int EPT, bool VEC>
-__global__ __launch_bounds__(kThreads) void topk_reg_kernel(TopkArgs a) {
+template <int EPT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t scan_sh[kWaves + 1];
+  __shared__ uint32_t scan_sh[NT / 64 + 1];
   __shared__ uint32_t ctrl[4];
 
   const int row = blockIdx.x;
@@ -178,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(TopkArgs a) {
   const int n = min(pos + 1, a.Lk);
   int32_t* out = a.indices + (size_t)row * a.k;
   if (n <= a.k) {
-    for (int i = threadIdx.x; i < a.k; i += kThreads) out[i] = i < n ? i : -1;
+    for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < n ? i : -1;
     return;
   }
   const float* srow = a.scores + (size_t)row * a.Lk;
@@ -205,19 +232,32 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(TopkArgs a) {
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < EPT; ++j)
       if (j < cnt && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
     __syncthreads();
-    const int b0 = kBins - 1 - 2 * (int)threadIdx.x, b1 = b0 - 1;
-    const uint32_t h0 = hist[b0], h1 = hist[b1];
+    // thread i owns bins kBins-1-BPT*i down to kBins-BPT*(i+1); a scan in
+    // descending bin order gives suffix counts
+    constexpr int BPT = kBins / NT;
+    uint32_t h[BPT], hs = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      h[e] = hist[kBins - 1 - BPT * (int)threadIdx.x - e];
+      hs += h[e];
+    }
     uint32_t total;
-    const uint32_t incl = block_inclusive_scan(h0 + h1, scan_sh, total);
-    const uint32_t excl = incl - h0 - h1;
-    if (excl < need && need <= excl + h0) { ctrl[0] = (uint32_t)b0; ctrl[1] = excl; }
-    if (excl + h0 < need && need <= incl) { ctrl[0] = (uint32_t)b1; ctrl[1] = excl + h0; }
+    const uint32_t incl = block_inclusive_scan_n<NT>(hs, scan_sh, total);
+    uint32_t above = incl - hs;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      if (above < need && need <= above + h[e]) {
+        ctrl[0] = (uint32_t)(kBins - 1 - BPT * (int)threadIdx.x - e);
+        ctrl[1] = above;
+      }
+      above += h[e];
+    }
     __syncthreads();
     const uint32_t d = ctrl[0];
     need -= ctrl[1];
@@ -240,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void topk_reg_kernel(TopkArgs a) {
   }
   uint32_t total;
   const uint32_t packed = gt | (eq << 16);
-  const uint32_t excl = block_inclusive_scan(packed, scan_sh, total) - packed;
+  const uint32_t excl = block_inclusive_scan_n<NT>(packed, scan_sh, total) - packed;
   uint32_t gt_before = excl & 0xFFFFu, eq_before = excl >> 16;
 #pragma unroll
   for (int j = 0; j < EPT; ++j) {
@@ -267,10 +307,10 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((long long)a.B * a.Lq));
   const int max_n = min(a.q_start + a.Lq, a.Lk);
   const size_t base = (size_t)(kBins + kWaves + 1 + 4) * sizeof(uint32_t);
-  if (max_n <= 32 * kThreads) {
+  if (max_n <= 64 * 512) {
     if (a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0)
-      return launch_kernel((const void*)topk_reg_kernel<32, true>, grid, dim3(kThreads), 0, stream, a);
-    return launch_kernel((const void*)topk_reg_kernel<32, false>, grid, dim3(kThreads), 0, stream, a);
+      return launch_kernel((const void*)topk_reg_kernel<64, true, 512>, grid, dim3(512), 0, stream, a);
+    return launch_kernel((const void*)topk_reg_kernel<64, false, 512>, grid, dim3(512), 0, stream, a);
   }
   if (max_n <= kCacheMax) {
     static const hipError_t attr = hipFuncSetAttribute(
