@@ -33,6 +33,7 @@ KERNEL_SOURCES = {
     "sparse_mla_attn": "sparse_attention_02_amd/csrc/sparse_mla.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+COPY_BYTES = 1 << 30  # calibration copy: reads and writes exactly this many bytes
 
 
 def parse():
@@ -44,6 +45,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain device-to-device copy of "
+                         f"{COPY_BYTES >> 20} MiB three times (reference dispatches for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters of a PMC run)")
     return ap.parse_args()
 
 
@@ -182,6 +187,16 @@ def main():
     wall = time.perf_counter() - t0
     print(f"[bench] {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
 
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] calibration copies of {COPY_BYTES} bytes done", file=sys.stderr, flush=True)
+
     per = {n: [] for n in names}
     for ev in events:
         for j, n in enumerate(names):
@@ -193,7 +208,7 @@ def main():
     kernels = {}
     for n in names:
         avg_ms = float(np.mean(per[n]))
-        k = {"avg_ms": avg_ms, "min_ms": float(np.min(per[n])),
+        k = {"avg_ms": avg_ms, "median_ms": float(np.median(per[n])), "min_ms": float(np.min(per[n])),
              "algorithmic_flop": work[n]["flop"], "algorithmic_bytes": work[n]["bytes"],
              "hbm_bytes_per_launch": traffic_for(n)}
         if work[n]["flop"]:
@@ -225,6 +240,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "event_ms_per_step": float(np.mean(step_ms)),
+        "event_ms_per_step_median": float(np.median(step_ms)),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

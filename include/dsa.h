@@ -69,7 +69,7 @@ typedef struct dsa_problem {
   int32_t kv_len;      /* Lk >= 1, q_start + q_len <= kv_len                    */
   int32_t q_start;     /* absolute position of query row 0 (>= 0)              */
   int32_t idx_heads;   /* H_I, 1..64                                           */
-  int32_t idx_dim;     /* d_I, multiple of 16, 16..128                         */
+  int32_t idx_dim;     /* d_I: 32, 64, 96 or 128                                */
   int32_t topk;        /* k, 1..2048                                           */
   int32_t heads;       /* H, 1..128                                            */
   int32_t d_latent;    /* D_v: 512, or 64 (with D_r = 16)                       */
