@@ -97,6 +97,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __builtin_assume(wave >= 0 && wave < NW);
   const int g = lane >> 4;
   const int li = lane & 15;
   const int row = blockIdx.x;
@@ -144,18 +145,32 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   const uint8_t* kv_seq = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK);
   auto issue = [&](int c, int buf) {
     uint8_t* dst = kvb + buf * S::CHUNK_BYTES;
+    constexpr int NJ = (S::DMA_BLOCKS + NW - 1) / NW;
+    // All row indices are read before the first copy is issued: the copies
+    // are asm statements with a memory clobber, so a look-up placed after one
+    // could not be hoisted and each block would pay a full LDS round trip.
+    // The lane offsets are recomputed per call (hoisting them out of the chunk
+    // loop would hold ~10 registers), and any spill reload here would make the
+    // compiler wait for every gather in flight.
+    int ln;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+    int idx[NJ];
 #pragma unroll
-    for (int j0 = 0; j0 < (S::DMA_BLOCKS + NW - 1) / NW; ++j0) {
+    for (int j0 = 0; j0 < NJ; ++j0) {
+      const int j = min(j0 * NW + wave, S::DMA_BLOCKS - 1);
+      idx[j0] = sidx[c * kChunk + (64 * j + ln) / S::PPR];
+    }
+#pragma unroll
+    for (int j0 = 0; j0 < NJ; ++j0) {
       const int j = j0 * NW + wave;
       if (j < S::DMA_BLOCKS) {
-        const int p = 64 * j + lane;
+        const int p = 64 * j + ln;
         const int r = p / S::PPR, pp = p % S::PPR;
         const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
-        const int idx = sidx[c * kChunk + r];
-        const int src_row = idx >= 0 ? idx : 0;
         const int src_col = lp < S::RPR ? lp : lp - S::RPR;  // pad pieces meet zero q
+        // row indices are < 2^24 (one sequence's cache is < 4 GiB)
         dma16(__builtin_amdgcn_readfirstlane(lds_offset(dst + 1024 * j)), kv_seq,
-              (uint32_t)src_row * (DQK * 2) + 16 * src_col);
+              __umul24((uint32_t)max(idx[j0], 0), DQK * 2) + 16 * src_col);
       }
     }
   };
