@@ -36,9 +36,21 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kQPW = 2;       // queries per wave
 constexpr int kKeysPerWave = 64;
-constexpr int kMaxHG = 4;     // head groups of 16 (H_I <= 64)
 
-template <int NKL>
+// NHG = number of 16-head groups (H_I <= 16 * NHG; absent heads have zero
+// queries and weights).  A compile-time count keeps the MFMA sequence free of
+// branches, so the 2 * NHG products of a key tile are issued back to back into
+// separate accumulators before their epilogues read them.
+// FULLD: d_I == 128, every lane group holds 32 bytes of the key row.
+// ReLU as a single v_max_f32.  This file is compiled without NaN semantics
+// (the scores of NaN inputs are undefined): with them, fmaxf(x, 0) costs two
+// VALU operations (a NaN-quieting canonicalisation of x, then the max), and
+// the epilogue's VALU work already matches the matrix work.  A zero of either
+// sign may come out; it only ever multiplies a head weight into a sum that
+// starts at +0.
+__device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.0f); }
+
+template <int NKL, int NHG, bool FULLD>
 __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
   constexpr int NQG = 4 / NKL;          // query groups per block
   constexpr int QT = kQPW * NQG;        // queries per block
@@ -68,20 +80,19 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
   const int dI = a.dI;
   const int row_bytes = dI + 16;        // padded LDS row
   const int stage_bytes = KS * row_bytes;
-  const int nhg = (a.HI + 15) >> 4;
   const bool g_active = 32 * g < dI;
 
   // ---- A operands (query heads) and head weights, resident for the whole block
-  v8i qa[kQPW][kMaxHG];
-  float wr[kQPW][kMaxHG][4];
+  v8i qa[kQPW][NHG];
+  float wr[kQPW][NHG][4];
 #pragma unroll
   for (int q = 0; q < kQPW; ++q) {
     const int t = t_first + qgroup * kQPW + q;
 #pragma unroll
-    for (int hg = 0; hg < kMaxHG; ++hg) {
+    for (int hg = 0; hg < NHG; ++hg) {
       const int head = 16 * hg + (lane & 15);
       v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (t < a.Lq && hg < nhg && head < a.HI && g_active) {
+      if (t < a.Lq && head < a.HI && g_active) {
         const uint8_t* src = a.q_idx + (((size_t)b * a.Lq + t) * a.HI + head) * dI + 32 * g;
         const v4i* s4 = (const v4i*)src;
         v4i lo = s4[0], hi = s4[1];
@@ -128,9 +139,6 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
   store_stage(0);
   __syncthreads();
 
-  const bool hi = (lane >> 5) & 1;
-  const bool mid = (lane >> 4) & 1;
-
   for (int st = st_begin; st < st_end; ++st) {
     const int buf = (st - st_begin) & 1;
     if (st + 1 < st_end) load_stage(st + 1);
@@ -145,39 +153,44 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int key_local = kKeysPerWave * klane + 16 * kt + (lane & 15);
-      v8i kb = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (g_active) {
-        const v4i* s4 = (const v4i*)(sb + key_local * row_bytes + 32 * g);
-        v4i lo = s4[0], hi4 = s4[1];
-        kb = (v8i){lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      }
+      // With d_I < 128 the lane groups past d_I read the row's first bytes and
+      // use zeros (stale bytes could be FP8 NaNs, and 0 * NaN is NaN).
+      const bool ld = FULLD || g_active;
+      const v4i* s4 = (const v4i*)(sb + key_local * row_bytes + (ld ? 32 * g : 0));
+      v4i lo = s4[0], hi4 = s4[1];
+      if (!FULLD && !g_active) lo = hi4 = (v4i){0, 0, 0, 0};
+      const v8i kb = (v8i){lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      v4f x[kQPW][NHG];
 #pragma unroll
-      for (int q = 0; q < kQPW; ++q) {
+      for (int q = 0; q < kQPW; ++q)
 #pragma unroll
-        for (int hg = 0; hg < kMaxHG; ++hg) {
-          if (hg < nhg) {
-            const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            const v4f x = mfma_f8_16x16x128(qa[q][hg], kb, zero);
+        for (int hg = 0; hg < NHG; ++hg)
+          x[q][hg] = mfma_f8_16x16x128(qa[q][hg], kb, (v4f){0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) part[q][kt] += wr[q][hg][r] * fmaxf(x[r], 0.0f);
-          }
-        }
-      }
+      for (int q = 0; q < kQPW; ++q)
+#pragma unroll
+        for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[q][kt] += wr[q][hg][r] * relu(x[q][hg][r]);
     }
 
     // ---- head-group reduction + key-tile spread, then the store
     const int key = st * KS + kKeysPerWave * klane + lane;
 #pragma unroll
     for (int q = 0; q < kQPW; ++q) {
-      const float s0 = hi ? part[q][0] : part[q][2];
-      const float s1 = hi ? part[q][1] : part[q][3];
-      const float r0 = __shfl_xor(s0, 32);
-      const float r1 = __shfl_xor(s1, 32);
-      const float k0 = (hi ? part[q][2] : part[q][0]) + r0;
-      const float k1 = (hi ? part[q][3] : part[q][1]) + r1;
-      const float snd = mid ? k0 : k1;
-      const float rcv = __shfl_xor(snd, 16);
-      const float fin = (mid ? k1 : k0) + rcv;
+      // v_permlane32_swap(x, y) trades the upper half of x for the lower half
+      // of y, so x' + y' is, in lanes 0..31, key tile 0 summed over lane groups
+      // g and g^2 and, in lanes 32..63, the same for tile 2 (tiles 1 and 3
+      // likewise).  permlane16_swap then adds groups g and g^1 and leaves
+      // lane l with key l of the stage.
+      const auto a02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[q][0]),
+                                                        __float_as_uint(part[q][2]), false, false);
+      const auto a13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[q][1]),
+                                                        __float_as_uint(part[q][3]), false, false);
+      const float k0 = __uint_as_float(a02[0]) + __uint_as_float(a02[1]);
+      const float k1 = __uint_as_float(a13[0]) + __uint_as_float(a13[1]);
+      const auto b01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
+      const float fin = __uint_as_float(b01[0]) + __uint_as_float(b01[1]);
       const int t = t_first + qgroup * kQPW + q;
       if (t < a.Lq && key <= a.q_start + t && key < a.Lk)
         a.scores[((size_t)b * a.Lq + t) * a.Lk + key] = fin;
@@ -204,13 +217,22 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
   a.n_splits = splits;
   const size_t smem = 2 * (size_t)KS * (a.dI + 16);
   const dim3 grid((unsigned)(tiles * splits));
-  if (decode) {
-    static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)index_scores_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  const int nhg = (a.HI + 15) >> 4;
+  const bool full = a.dI == 128;
+#define DSA_K1(NKL, NHG) \
+  (full ? (const void*)index_scores_kernel<NKL, NHG, true> : (const void*)index_scores_kernel<NKL, NHG, false>)
+  const void* kern;
+  if (decode)
+    kern = nhg == 1 ? DSA_K1(4, 1) : nhg == 2 ? DSA_K1(4, 2) : DSA_K1(4, 4);
+  else
+    kern = nhg == 1 ? DSA_K1(1, 1) : nhg == 2 ? DSA_K1(1, 2) : DSA_K1(1, 4);
+#undef DSA_K1
+  if (smem > 64 * 1024) {
+    const hipError_t attr =
+        hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    return launch_kernel((const void*)index_scores_kernel<4>, grid, dim3(kThreads), smem, stream, a);
   }
-  return launch_kernel((const void*)index_scores_kernel<1>, grid, dim3(kThreads), smem, stream, a);
+  return launch_kernel(kern, grid, dim3(kThreads), smem, stream, a);
 }
 
 }  // namespace dsa
