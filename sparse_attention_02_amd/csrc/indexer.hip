@@ -17,10 +17,14 @@
 //
 // Work split.  A block of 4 waves owns a tile of consecutive query rows of one
 // sequence and walks the keys 0 .. (last position of the tile) in stages:
-//  - prefill (NKL = 1): 4 query groups x 2 queries; every wave reads the same
-//    64-key stage from LDS, so each key byte fetched from L2 feeds 8 queries.
-//  - decode  (NKL = 4): 1 query group; the 4 waves take 4 different 64-key
-//    slices of a 256-key stage (there is nothing to share between queries).
+//  - prefill (NKL = 1): 4 waves x 1 query; every wave reads the same 64-key
+//    stage from LDS, so each key byte fetched from L2 feeds 4 queries.  One
+//    query per wave keeps a wave at ~96 registers, so 5 waves share a SIMD
+//    and hide each other's MFMA -> epilogue latency (the epilogue's VALU work
+//    is as long as the MFMA work, so neither pipe may wait on the other).
+//  - decode  (NKL = 4): 4 waves x 2 queries of one query group; the waves take
+//    4 different 64-key slices of a 256-key stage (nothing to share between
+//    queries).
 // Key stages are double-buffered in LDS; the next stage's global loads are in
 // flight while the current one is multiplied.  The causal triangle is skipped
 // at stage granularity; keys past a row's position are computed but not
@@ -33,8 +37,8 @@ namespace dsa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kQPW = 2;       // queries per wave
+constexpr int kPrefillWaves = 4, kPrefillQPW = 1;
+constexpr int kDecodeWaves = 4, kDecodeQPW = 2;
 constexpr int kKeysPerWave = 64;
 
 // NHG = number of 16-head groups (H_I <= 16 * NHG; absent heads have zero
@@ -50,9 +54,10 @@ constexpr int kKeysPerWave = 64;
 // starts at +0.
 __device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.0f); }
 
-template <int NKL, int NHG, bool FULLD>
-__global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
-  constexpr int NQG = 4 / NKL;          // query groups per block
+template <int NKL, int NHG, bool FULLD, int NW, int kQPW>
+__global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
+  constexpr int kThreads = 64 * NW;
+  constexpr int NQG = NW / NKL;         // query groups per block
   constexpr int QT = kQPW * NQG;        // queries per block
   constexpr int KS = kKeysPerWave * NKL;  // keys per stage
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void index_scores_kernel(IndexArgs a) {
 hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
   IndexArgs a = args_in;
   const bool decode = a.Lq < 8;
-  const int QT = decode ? kQPW : kQPW * 4;
+  const int QT = decode ? kDecodeQPW * kDecodeWaves / 4 : kPrefillQPW * kPrefillWaves;
   const int KS = decode ? 4 * kKeysPerWave : kKeysPerWave;
   a.n_qtiles = (a.Lq + QT - 1) / QT;
   // Split long key ranges until there are enough blocks to fill the chip.
@@ -219,20 +224,29 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
   const dim3 grid((unsigned)(tiles * splits));
   const int nhg = (a.HI + 15) >> 4;
   const bool full = a.dI == 128;
-#define DSA_K1(NKL, NHG) \
-  (full ? (const void*)index_scores_kernel<NKL, NHG, true> : (const void*)index_scores_kernel<NKL, NHG, false>)
+#define DSA_K1(NKL, NHG, NW, QPW)                                    \
+  (full ? (const void*)index_scores_kernel<NKL, NHG, true, NW, QPW> \
+        : (const void*)index_scores_kernel<NKL, NHG, false, NW, QPW>)
   const void* kern;
-  if (decode)
-    kern = nhg == 1 ? DSA_K1(4, 1) : nhg == 2 ? DSA_K1(4, 2) : DSA_K1(4, 4);
-  else
-    kern = nhg == 1 ? DSA_K1(1, 1) : nhg == 2 ? DSA_K1(1, 2) : DSA_K1(1, 4);
+  int threads;
+  if (decode) {
+    threads = 64 * kDecodeWaves;
+    kern = nhg == 1   ? DSA_K1(4, 1, kDecodeWaves, kDecodeQPW)
+           : nhg == 2 ? DSA_K1(4, 2, kDecodeWaves, kDecodeQPW)
+                      : DSA_K1(4, 4, kDecodeWaves, kDecodeQPW);
+  } else {
+    threads = 64 * kPrefillWaves;
+    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW)
+           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW)
+                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW);
+  }
 #undef DSA_K1
   if (smem > 64 * 1024) {
     const hipError_t attr =
         hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
   }
-  return launch_kernel(kern, grid, dim3(kThreads), smem, stream, a);
+  return launch_kernel(kern, grid, dim3(threads), smem, stream, a);
 }
 
 }  // namespace dsa
