@@ -109,7 +109,11 @@ int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* 
  *   scores  [B, Lq, Lk] float32 (as written by dsa_index_scores)
  *   indices [B, Lq, k]  int32 output
  *   workspace: device scratch of at least dsa_workspace_size(p, DSA_OP_TOPK)
- *              bytes (may be NULL when that size is 0).
+ *              bytes, 16-byte aligned (may be NULL when that size is 0).  It
+ *              is non-zero when rows can exceed 32768 candidates: such rows are
+ *              selected in two stages (top k of each 8192-key segment, then of
+ *              their union), with B*Lq*ceil(max_row/8192)*k*8 bytes of
+ *              candidates in between.  Contents on return are unspecified.
  */
 int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
              size_t workspace_bytes, void* stream);

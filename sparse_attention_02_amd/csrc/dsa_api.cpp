@@ -102,9 +102,9 @@ dsa::IndexArgs index_args(const dsa_problem* p, const uint8_t* q_idx, const uint
   return a;
 }
 
-dsa::TopkArgs topk_args(const dsa_problem* p, const float* scores, int32_t* indices) {
+dsa::TopkArgs topk_args(const dsa_problem* p, const float* scores, int32_t* indices, void* ws) {
   dsa::TopkArgs a{};
-  a.scores = scores; a.indices = indices;
+  a.scores = scores; a.indices = indices; a.workspace = ws;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start; a.k = p->topk;
   return a;
 }
@@ -146,13 +146,13 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       return check_index(p) ? bad : 0;
     case DSA_OP_TOPK:
       if (check_topk(p)) return bad;
-      return dsa::topk_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk);
+      return dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
     case DSA_OP_SPARSE_MLA_ATTN:
       return check_attn(p) ? bad : 0;
     case DSA_OP_FORWARD:
       if (check_index(p) || check_attn(p)) return bad;
       return round_up(scores_bytes(p)) + round_up(indices_bytes(p)) +
-             round_up(dsa::topk_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk));
+             round_up(dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk));
     default:
       fail(DSA_ERR_SHAPE, "unknown op %d", op);
       return bad;
@@ -178,10 +178,13 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
   if (int s = check_topk(p)) return s;
   if (int s = check_ptr(scores, "scores", 4)) return s;
   if (int s = check_ptr(indices, "indices", 4)) return s;
-  const size_t need = dsa::topk_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk);
+  const size_t need = dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
-  return hip_status(dsa::launch_topk(topk_args(p, scores, indices), (hipStream_t)stream),
+  if (need > 0 && !aligned(workspace, 16))
+    return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  return hip_status(dsa::launch_topk(topk_args(p, scores, indices, need > 0 ? workspace : nullptr),
+                                     (hipStream_t)stream),
                     "topk launch");
 }
 
@@ -227,8 +230,8 @@ int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx
   if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
                          "index_scores launch"))
     return s;
-  (void)topk_ws;
-  if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel), st), "topk launch")) return s;
+  if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel, topk_ws), st), "topk launch"))
+    return s;
   return hip_status(dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse), st),
                     "sparse_mla_attn launch");
 }

@@ -20,7 +20,12 @@ struct IndexArgs {
 struct TopkArgs {
   const float* scores;  // [B, Lq, Lk]
   int32_t* indices;     // [B, Lq, k]
+  void* workspace;      // topk_workspace_bytes() bytes, or null when that is 0
   int B, Lq, Lk, q_start, k;
+  // filled by the launcher for the two-stage path
+  int nseg;
+  uint32_t* cand_key;   // [B*Lq, nseg, k]
+  int32_t* cand_idx;    // [B*Lq, nseg, k]
 };
 
 struct AttnArgs {
@@ -44,7 +49,7 @@ inline hipError_t launch_kernel(const void* kernel, dim3 grid, dim3 block, size_
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
-size_t topk_workspace_bytes(int B, int Lq, int Lk, int k);
+size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k);
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace dsa

@@ -108,6 +108,43 @@ def test_topk_ties_and_signed_zero(dsa):
     np.testing.assert_array_equal(idx.cpu().numpy().reshape(Lq, k), ref)
 
 
+@pytest.mark.parametrize("k,Lk,Lq", [(64, 40000, 6), (2048, 40000, 4), (100, 65536, 3)])
+def test_topk_two_stage_long_rows(dsa, k, Lk, Lq):
+    """Rows longer than one block holds go through per-segment selection and a
+    merge; quantised scores put ties across segment boundaries, one row ends
+    exactly on a segment boundary and one just after it."""
+    rng = np.random.default_rng(k + Lk)
+    B = 2
+    q_start = Lk - Lq
+    wl = dsa_inputs.Workload("long", 0, B, Lq, Lk, q_start, 4, 32, k, 8, 64, 16)
+    s = rng.integers(-40, 41, size=(B, Lq, Lk)).astype(np.float32) * 0.25
+    s[0, 0, 8192 - 5:8192 + 5] = 10.0   # a tie straddling the first segment boundary
+    s[1, -1, :] = 3.0                    # an all-equal row: the k lowest indices win
+    prob = dsa.Problem.from_workload(wl)
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
+    assert ws_bytes > 0
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Lq, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(prob, dev(s), idx, ws, ws_bytes)
+    torch.cuda.synchronize()
+    pos = (q_start + np.arange(Lq)).astype(np.int32)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        ref = oracle.topk(np.ascontiguousarray(s[b]), pos, k)
+        np.testing.assert_array_equal(got[b], ref)
+    np.testing.assert_array_equal(got[1, -1], np.arange(k))
+
+
+def test_topk_two_stage_needs_workspace(dsa):
+    wl = dsa_inputs.Workload("long", 0, 1, 2, 40000, 39998, 4, 32, 64, 8, 64, 16)
+    prob = dsa.Problem.from_workload(wl)
+    scores = torch.zeros((1, 2, 40000), dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, 2, 64), dtype=torch.int32, device="cuda")
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_topk(prob, scores, idx)
+    assert e.value.status == -4
+
+
 def test_attention_invalid_entries_and_empty_rows(dsa):
     wl = dsa_inputs.Workload("inv", 21, 1, 6, 120, 114, 4, 32, 64, 16, 64, 16)
     inp = Inputs.make(wl)
