@@ -157,6 +157,8 @@ def main():
     lse = torch.empty((B, Lq, wl.heads), dtype=torch.float32, device=dev)
     ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    aws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
+    aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     names = ["index_scores", "topk", "sparse_mla_attn"]
@@ -170,7 +172,7 @@ def main():
         dsa.dsa_topk(prob, scores, indices, ws, ws_bytes, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, stream=stream)
+        dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 

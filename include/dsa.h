@@ -134,11 +134,19 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
  *   indices [B, Lq, k]       int32
  *   out     [B, Lq, H, D_v]  float32 output
  *   lse     [B, Lq, H]       float32 output, or NULL
+ *   workspace: optional device scratch, 16-byte aligned.  When it holds at
+ *              least dsa_workspace_size(p, DSA_OP_SPARSE_MLA_ATTN) bytes and
+ *              that size is non-zero (fewer query rows than compute units),
+ *              each row's selected entries are split over several blocks whose
+ *              normalised partial results (and their lse) are merged by a second
+ *              kernel; otherwise (NULL, or too small) one block handles a row.
+ *              Results agree within rounding either way.
  * Scores and the softmax run in fp32; the probabilities are rounded to bf16
  * for the value product on bf16 matrix cores with fp32 accumulation.
  */
 int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
-                        const int32_t* indices, float* out, float* lse, void* stream);
+                        const int32_t* indices, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream);
 
 /*
  * dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.

@@ -76,7 +76,7 @@ def _load():
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     L.dsa_index_scores.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
-    L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_forward):
         f.restype = i32
@@ -136,10 +136,15 @@ def dsa_topk(problem: Problem, scores, indices, workspace=None, workspace_bytes:
                         workspace_bytes, _stream(stream)))
 
 
-def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:
-    """Sparse MQA-mode attention over the selected latents (include/dsa.h: dsa_sparse_mla_attn)."""
+def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, workspace=None,
+                        workspace_bytes: int = 0, stream=None) -> None:
+    """Sparse MQA-mode attention over the selected latents (include/dsa.h: dsa_sparse_mla_attn).
+    The workspace is optional (see dsa_workspace_size(problem, DSA_OP_SPARSE_MLA_ATTN))."""
+    if workspace is not None and not isinstance(workspace, int) and workspace_bytes == 0:
+        workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_mla_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
-                                   _ptr(out), _ptr(lse), _stream(stream)))
+                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
+                                   _stream(stream)))
 
 
 def dsa_forward(problem: Problem, q_idx, k_idx, w, q, kv, out, lse=None, indices=None,

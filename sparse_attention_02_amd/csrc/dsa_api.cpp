@@ -109,13 +109,26 @@ dsa::TopkArgs topk_args(const dsa_problem* p, const float* scores, int32_t* indi
   return a;
 }
 
+size_t attn_ws_bytes(const dsa_problem* p) {
+  return dsa::attn_workspace_bytes(p->batch * p->q_len, p->topk, p->heads, p->d_latent);
+}
+
+// The chunk split is used when the workspace can hold its partial results.
 dsa::AttnArgs attn_args(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
-                        const int32_t* indices, float* out, float* lse) {
+                        const int32_t* indices, float* out, float* lse, void* ws, size_t ws_bytes) {
   dsa::AttnArgs a{};
   a.q = q; a.kv = kv; a.indices = indices; a.out = out; a.lse = lse;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.H = p->heads;
   a.Dv = p->d_latent; a.Dr = p->d_rope; a.k = p->topk;
   a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a.nsplit = 1;
+  const size_t need = attn_ws_bytes(p);
+  if (need > 0 && ws && ws_bytes >= need) {
+    const size_t rows = (size_t)p->batch * p->q_len;
+    a.nsplit = dsa::attn_splits((int)rows, p->topk);
+    a.part_out = (float*)ws;
+    a.part_lse = a.part_out + rows * a.nsplit * p->heads * p->d_latent;
+  }
   return a;
 }
 
@@ -148,11 +161,12 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       if (check_topk(p)) return bad;
       return dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
     case DSA_OP_SPARSE_MLA_ATTN:
-      return check_attn(p) ? bad : 0;
+      return check_attn(p) ? bad : attn_ws_bytes(p);
     case DSA_OP_FORWARD:
       if (check_index(p) || check_attn(p)) return bad;
       return round_up(scores_bytes(p)) + round_up(indices_bytes(p)) +
-             round_up(dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk));
+             round_up(dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk)) +
+             round_up(attn_ws_bytes(p));
     default:
       fail(DSA_ERR_SHAPE, "unknown op %d", op);
       return bad;
@@ -189,7 +203,8 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
 }
 
 int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
-                        const int32_t* indices, float* out, float* lse, void* stream) {
+                        const int32_t* indices, float* out, float* lse, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (int s = check_common(p)) return s;
   if (int s = check_attn(p)) return s;
   if (int s = check_ptr(q, "q", 16)) return s;
@@ -197,8 +212,10 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
   if (int s = check_ptr(indices, "indices", 16)) return s;
   if (int s = check_ptr(out, "out", 16)) return s;
   if (lse && !aligned(lse, 4)) return fail(DSA_ERR_ALIGN, "lse is not 4-byte aligned");
-  return hip_status(dsa::launch_sparse_mla_attn(attn_args(p, q, kv, indices, out, lse),
-                                                (hipStream_t)stream),
+  if (workspace && !aligned(workspace, 16)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  return hip_status(dsa::launch_sparse_mla_attn(
+                        attn_args(p, q, kv, indices, out, lse, workspace, workspace_bytes),
+                        (hipStream_t)stream),
                     "sparse_mla_attn launch");
 }
 
@@ -225,6 +242,9 @@ int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx
   float* scores = (float*)ws;
   int32_t* sel = indices ? indices : (int32_t*)(ws + round_up(scores_bytes(p)));
   void* topk_ws = ws + round_up(scores_bytes(p)) + round_up(indices_bytes(p));
+  const size_t topk_bytes =
+      dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
+  void* attn_ws = (uint8_t*)topk_ws + round_up(topk_bytes);
   hipStream_t st = (hipStream_t)stream;
 
   if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
@@ -232,8 +252,9 @@ int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx
     return s;
   if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel, topk_ws), st), "topk launch"))
     return s;
-  return hip_status(dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse), st),
-                    "sparse_mla_attn launch");
+  return hip_status(
+      dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse, attn_ws, attn_ws_bytes(p)), st),
+      "sparse_mla_attn launch");
 }
 
 }  // extern "C"

@@ -36,6 +36,12 @@ struct AttnArgs {
   float* lse;               // [B, Lq, H] or null
   int B, Lq, Lk, H, Dv, Dr, k;
   float scale_log2;         // softmax_scale * log2(e)
+  // split over the selected chunks (nsplit > 1): block (row, part) writes the
+  // attention over its share of the chunks, normalised, with its lse, to
+  // part_out [B*Lq, nsplit, H, Dv] and part_lse [B*Lq, nsplit, H]
+  int nsplit;
+  float* part_out;
+  float* part_lse;
 };
 
 // Launch `kernel(arg)` and return the launch's own status (not the thread's
@@ -51,5 +57,9 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k);
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream);
+// Parts per row when few rows would leave most CUs idle (1: no split), and the
+// workspace the split needs.
+int attn_splits(int rows, int k);
+size_t attn_workspace_bytes(int rows, int k, int H, int Dv);
 
 }  // namespace dsa

@@ -100,21 +100,29 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   __builtin_assume(wave >= 0 && wave < NW);
   const int g = lane >> 4;
   const int li = lane & 15;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / a.nsplit;
+  const int part = blockIdx.x % a.nsplit;
   const int b = row / a.Lq;
   const int nch = (a.k + kChunk - 1) / kChunk;
+  // chunks [c_lo, c_hi) of the row belong to this block
+  const int c_lo = part * nch / a.nsplit, c_hi = (part + 1) * nch / a.nsplit;
+  float* out_base = a.nsplit > 1 ? a.part_out + (size_t)blockIdx.x * a.H * DV
+                                 : a.out + (size_t)row * a.H * DV;
+  float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)blockIdx.x * a.H
+                                 : (a.lse ? a.lse + (size_t)row * a.H : nullptr);
 
   // ---- selected indices -> LDS (entries outside [0, Lk) become -1)
   const int32_t* idx_row = a.indices + (size_t)row * a.k;
-  for (int i = threadIdx.x; i < nch * kChunk; i += blockDim.x) {
+  for (int i = c_lo * kChunk + threadIdx.x; i < c_hi * kChunk; i += blockDim.x) {
     const int v = i < a.k ? idx_row[i] : -1;
     sidx[i] = (v >= 0 && v < a.Lk) ? v : -1;
   }
   __syncthreads();
   uint64_t chunk_mask, full_mask;  // chunks with some / with only valid entries
   {
-    bool any = false, all = lane < nch;
-    if (lane < nch)
+    const bool mine = lane >= c_lo && lane < c_hi;
+    bool any = false, all = mine;
+    if (mine)
       for (int j = 0; j < kChunk; ++j) {
         const bool v = sidx[lane * kChunk + j] >= 0;
         any |= v;
@@ -359,9 +367,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     const int head = 16 * (S::HTQ * wave + ht) + li;
     if (g == 0) {
       lsum_s[head] = l;
-      if (a.lse && head < a.H)
-        a.lse[(size_t)row * a.H + head] =
-            l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
+      if (lse_base && head < a.H)
+        lse_base[head] = l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
     }
   }
   __syncthreads();
@@ -373,13 +380,39 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     if (head < a.H) {
       const float l = lsum_s[head];
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      float* orow = a.out + ((size_t)row * a.H + head) * DV;
+      float* orow = out_base + (size_t)head * DV;
 #pragma unroll
       for (int dt = 0; dt < S::DTW; ++dt) {
         const int d0 = 16 * (wave * S::DTW + dt) + 4 * g;
         *(v4f*)(orow + d0) = acc[ht][dt] * inv;
       }
     }
+  }
+}
+
+// Merge of the parts of split rows: lse = log(sum_p exp(lse_p)) and
+// out = sum_p exp(lse_p - lse) * out_p (each part is normalised by its own
+// softmax sum); a row without any valid entry keeps out = 0, lse = -inf.
+// One block per (row, head), one 4-column group per thread.
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  const int rh = blockIdx.x;  // row * H + head
+  const int row = rh / a.H, head = rh % a.H;
+  const float* lp = a.part_lse + (size_t)row * a.nsplit * a.H + head;
+  float m = -INFINITY;
+  for (int p = 0; p < a.nsplit; ++p) m = fmaxf(m, lp[(size_t)p * a.H]);
+  float sum = 0.0f;
+  for (int p = 0; p < a.nsplit; ++p) sum += m == -INFINITY ? 0.0f : __expf(lp[(size_t)p * a.H] - m);
+  const float lse = sum > 0.0f ? m + __logf(sum) : -INFINITY;
+  if (threadIdx.x == 0 && a.lse) a.lse[rh] = lse;
+  for (int d4 = threadIdx.x; d4 < a.Dv / 4; d4 += blockDim.x) {
+    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int p = 0; p < a.nsplit; ++p) {
+      const float lpp = lp[(size_t)p * a.H];
+      if (lpp == -INFINITY) continue;
+      const float wgt = __expf(lpp - lse);
+      o += wgt * *(const v4f*)(a.part_out + (((size_t)row * a.nsplit + p) * a.H + head) * a.Dv + 4 * d4);
+    }
+    *(v4f*)(a.out + (size_t)rh * a.Dv + 4 * d4) = o;
   }
 }
 
@@ -393,11 +426,32 @@ hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
       (const void*)sparse_mla_kernel<DQK, DV, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
       160 * 1024);
   if (attr != hipSuccess) return attr;
-  return launch_kernel((const void*)sparse_mla_kernel<DQK, DV, NW>,
-                       dim3((unsigned)((long long)a.B * a.Lq)), dim3(64 * NW), smem, stream, a);
+  const long long rows = (long long)a.B * a.Lq;
+  const hipError_t e = launch_kernel((const void*)sparse_mla_kernel<DQK, DV, NW>,
+                                     dim3((unsigned)(rows * a.nsplit)), dim3(64 * NW), smem, stream, a);
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  return launch_kernel((const void*)attn_combine_kernel, dim3((unsigned)(rows * a.H)), dim3(128), 0,
+                       stream, a);
 }
 
 }  // namespace
+
+int attn_splits(int rows, int k) {
+  // one block per CU at a time (the chunk ring fills most of the LDS): split
+  // the chunks of a row when there are fewer rows than CUs
+  constexpr int kCUs = 256;
+  const int nch = (k + kChunk - 1) / kChunk;
+  if (rows >= kCUs || nch < 4) return 1;
+  int ns = kCUs / rows;
+  if (ns > 8) ns = 8;
+  if (ns > nch / 2) ns = nch / 2;
+  return ns < 1 ? 1 : ns;
+}
+
+size_t attn_workspace_bytes(int rows, int k, int H, int Dv) {
+  const int ns = attn_splits(rows, k);
+  return ns > 1 ? (size_t)rows * ns * H * (Dv + 1) * sizeof(float) : 0;
+}
 
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.Dv == 512 && a.Dr == 64) return launch_shape<576, 512, 8>(a, stream);

@@ -55,7 +55,9 @@ def run_stages(prob, d, wl, fill_scores=float("-inf"), lse=True):
     ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     dsa.dsa_topk(prob, scores, indices, ws, ws_bytes)
-    dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], indices, out, lse_t)
+    aws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
+    aws = torch.empty(aws_bytes, dtype=torch.uint8, device="cuda") if aws_bytes else None
+    dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], indices, out, lse_t, aws, aws_bytes)
     torch.cuda.synchronize()
     return scores, indices, out, lse_t
 

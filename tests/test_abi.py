@@ -98,6 +98,12 @@ def test_null_and_alignment():
 def test_workspace_sizes_and_forward_checks():
     assert dsa.workspace_size(GOOD, dsa.DSA_OP_INDEX_SCORES) == 0
     assert dsa.workspace_size(GOOD, dsa.DSA_OP_TOPK) == 0
+    assert dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN) == 0
+    # few long rows: the top-k splits rows into segments, the attention splits
+    # each row's entries over blocks; both need scratch
+    dec = Problem(64, 1, 131072, 131071, 64, 128, 2048, 128, 512, 64)
+    assert dsa.workspace_size(dec, dsa.DSA_OP_TOPK) == 64 * 16 * 2048 * 8
+    assert dsa.workspace_size(dec, dsa.DSA_OP_SPARSE_MLA_ATTN) == 64 * 4 * 128 * 513 * 4
     ws = dsa.workspace_size(MLA, dsa.DSA_OP_FORWARD)
     scores = 4096 * 4096 * 4
     idx = 4096 * 2048 * 4

@@ -145,6 +145,40 @@ def test_topk_two_stage_needs_workspace(dsa):
     assert e.value.status == -4
 
 
+def test_attention_split_matches_unsplit(dsa):
+    """Few rows (decode-like): with a workspace each row's entries are split over
+    several blocks and merged; the result matches the oracle and the unsplit path."""
+    B, Lk, k = 6, 5000, 2048
+    wl = dsa_inputs.Workload("split", 31, B, 1, Lk, Lk - 1, 4, 32, k, 128, 512, 64)
+    inp = Inputs.make(wl)
+    rng = np.random.default_rng(5)
+    idx = np.full((B, 1, k), -1, np.int32)
+    for b in range(B - 1):
+        n = [k, 1500, 37, k, 900][b]
+        idx[b, 0, :n] = np.sort(rng.choice(Lk, n, replace=False))
+    # the last row has no valid entry
+    prob = dsa.Problem.from_workload(wl)
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
+    assert ws_bytes > 0
+    d = inp.device()
+    outs = []
+    for use_ws in (True, False):
+        out = torch.empty((B, 1, 128, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, 1, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if use_ws else None
+        dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], dev(idx), out, lse, ws, ws_bytes if use_ws else 0)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy()[:, 0], lse.cpu().numpy()[:, 0]))
+    rb = np.arange(B, dtype=np.int32)
+    ref_o, ref_l = oracle.sparse_mla_attn(inp.kv, inp.q, idx[:, 0], rb, 512, wl.softmax_scale)
+    for o, l in outs:
+        assert np.abs(o - ref_o).max() <= ATOL
+        fin = np.isfinite(ref_l)
+        assert np.abs(l[fin] - ref_l[fin]).max() <= ATOL
+        assert (o[-1] == 0).all() and np.isneginf(l[-1]).all()
+    assert np.abs(outs[0][0] - outs[1][0]).max() <= 2e-3
+
+
 def test_attention_invalid_entries_and_empty_rows(dsa):
     wl = dsa_inputs.Workload("inv", 21, 1, 6, 120, 114, 4, 32, 64, 16, 64, 16)
     inp = Inputs.make(wl)
