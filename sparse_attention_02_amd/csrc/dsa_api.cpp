@@ -69,9 +69,12 @@ int check_attn(const dsa_problem* p) {
     return fail(DSA_ERR_UNSUPPORTED, "latent shape %d + %d: supported 512 + 64 and 64 + 16",
                 p->d_latent, p->d_rope);
   // the latent gather addresses one sequence's cache with 32-bit byte offsets
-  if ((long long)p->kv_len * (p->d_latent + p->d_rope) * 2 >= (1LL << 32))
-    return fail(DSA_ERR_UNSUPPORTED, "kv_len %d: one sequence's latent cache must be < 4 GiB",
-                p->kv_len);
+  // (plus a few KiB of bias) and multiplies row indices in 24 bits
+  if ((long long)p->kv_len * (p->d_latent + p->d_rope) * 2 > (1LL << 32) - 8192 ||
+      p->kv_len > (1 << 24))
+    return fail(DSA_ERR_UNSUPPORTED,
+                "kv_len %d: the latent gather needs kv_len <= 2^24 and one sequence's cache "
+                "below 4 GiB - 8 KiB", p->kv_len);
   return DSA_OK;
 }
 

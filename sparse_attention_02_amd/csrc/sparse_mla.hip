@@ -58,8 +58,6 @@ struct AttnShape {
   static constexpr int CHUNK_BYTES = kChunk * RS;
   static constexpr int DMA_BLOCKS = CHUNK_BYTES / 1024;  // 64 lanes x 16 bytes
   static constexpr bool SWZ = PPR % 8 == 0;
-  static constexpr int DMA_LO = DMA_BLOCKS / NW;    // DMA blocks of waves >= DMA_BLOCKS % NW
-  static constexpr int DMA_HI_WAVES = DMA_BLOCKS % NW;
   static constexpr int P_BYTES = 128 * kPRow;
   static_assert(CHUNK_BYTES % 1024 == 0, "chunk must be whole 1 KiB DMA blocks");
   static_assert(HTQ >= 1 && HTQ * 16 * NW == 128, "score heads must tile 128");
@@ -70,14 +68,43 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// 16-byte global -> LDS copy of lane i from (base + offset_i) to (m0 + 16 i).
-// Issued through inline assembly so that the compiler does not insert a
-// conservative wait for it before every later LDS read; completion is tracked
-// with explicit vmcnt waits.  `base` is wave-uniform (SGPR pair).
-__device__ __forceinline__ void dma16(uint32_t lds_base, const void* base, uint32_t offset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_base), "v"(offset), "s"(base) : "memory");
+// N 1 KiB global -> LDS copies: copy n moves 16 bytes per lane i from
+// (base + off[n]_i + o_n) to (lds_mid + o_n + 16 i) with o_n = 1024 * (n - 2).
+// The instruction's immediate offset moves the LDS destination as well as the
+// global source, so one M0 write serves the whole run; rewriting M0 stalls the
+// wave while its earlier LDS operations drain, which made a write per copy the
+// largest cost of the gather.  Issued through inline assembly so that the
+// compiler does not insert a conservative wait for the copies before every
+// later LDS read; completion is tracked with explicit vmcnt waits.  `base` is
+// wave-uniform (SGPR pair).
+#define DSA_DMA(i, o) "global_load_lds_dwordx4 %" #i ", %5 offset:" #o "\n\t"
+template <int N>
+__device__ __forceinline__ void dma_run(uint32_t lds_mid, const void* base, const uint32_t (&off)[5]) {
+  static_assert(N >= 1 && N <= 5, "1 to 5 copies per run");
+  if constexpr (N == 5)
+    asm volatile("s_mov_b32 m0, %6\n\ts_nop 0\n\t" DSA_DMA(0, -2048) DSA_DMA(1, -1024) DSA_DMA(2, 0)
+                 DSA_DMA(3, 1024) DSA_DMA(4, 2048)
+                 :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "s"(base), "s"(lds_mid)
+                 : "memory", "m0");
+  else if constexpr (N == 4)
+    asm volatile("s_mov_b32 m0, %6\n\ts_nop 0\n\t" DSA_DMA(0, -2048) DSA_DMA(1, -1024) DSA_DMA(2, 0)
+                 DSA_DMA(3, 1024)
+                 :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "s"(base), "s"(lds_mid)
+                 : "memory", "m0");
+  else if constexpr (N == 3)
+    asm volatile("s_mov_b32 m0, %6\n\ts_nop 0\n\t" DSA_DMA(0, -2048) DSA_DMA(1, -1024) DSA_DMA(2, 0)
+                 :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "s"(base), "s"(lds_mid)
+                 : "memory", "m0");
+  else if constexpr (N == 2)
+    asm volatile("s_mov_b32 m0, %6\n\ts_nop 0\n\t" DSA_DMA(0, -2048) DSA_DMA(1, -1024)
+                 :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "s"(base), "s"(lds_mid)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %6\n\ts_nop 0\n\t" DSA_DMA(0, -2048)
+                 :: "v"(off[0]), "v"(off[1]), "v"(off[2]), "v"(off[3]), "v"(off[4]), "s"(base), "s"(lds_mid)
+                 : "memory", "m0");
 }
+#undef DSA_DMA
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -149,38 +176,40 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     }
   }
 
-  // ---- gather of one chunk: this wave's 1 KiB DMA blocks
-  const uint8_t* kv_seq = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK);
+  // ---- gather of one chunk: this wave copies the 1 KiB blocks [j_lo, j_lo + n_j)
+  // of the chunk (4 or 5 for the 576-wide rows), so one M0 value (the LDS
+  // address of block j_lo + 2) and immediate offsets -2048..2048 reach them all.
+  // The global base sits 4 KiB below the sequence's cache so that the per-lane
+  // offsets, which absorb the immediate, stay non-negative.
+  const uint8_t* kv_bias = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK) - 4096;
+  constexpr int NJ = (S::DMA_BLOCKS + NW - 1) / NW;
+  static_assert(NJ <= 5 && S::DMA_BLOCKS / NW >= 1, "1 to 5 copies per wave and chunk");
+  const int j_lo = wave * S::DMA_BLOCKS / NW;
+  const bool long_run = (wave + 1) * S::DMA_BLOCKS / NW - j_lo == NJ;
   auto issue = [&](int c, int buf) {
-    uint8_t* dst = kvb + buf * S::CHUNK_BYTES;
-    constexpr int NJ = (S::DMA_BLOCKS + NW - 1) / NW;
-    // All row indices are read before the first copy is issued: the copies
-    // are asm statements with a memory clobber, so a look-up placed after one
-    // could not be hoisted and each block would pay a full LDS round trip.
+    // All row indices are read before the copies are issued: the copies are
+    // one asm statement with a memory clobber, so no look-up can move past it.
     // The lane offsets are recomputed per call (hoisting them out of the chunk
     // loop would hold ~10 registers), and any spill reload here would make the
     // compiler wait for every gather in flight.
     int ln;
     asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-    int idx[NJ];
+    uint32_t off[5] = {0, 0, 0, 0, 0};
 #pragma unroll
     for (int j0 = 0; j0 < NJ; ++j0) {
-      const int j = min(j0 * NW + wave, S::DMA_BLOCKS - 1);
-      idx[j0] = sidx[c * kChunk + (64 * j + ln) / S::PPR];
+      const int j = min(j_lo + j0, S::DMA_BLOCKS - 1);
+      const int p = 64 * j + ln;
+      const int r = p / S::PPR, pp = p % S::PPR;
+      const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
+      const int src_col = lp < S::RPR ? lp : lp - S::RPR;  // pad pieces meet zero q
+      const int idx = max(sidx[c * kChunk + r], 0);
+      // row indices are < 2^24 and the cache is < 4 GiB - 8 KiB (checked by the host)
+      off[j0] = __umul24((uint32_t)idx, DQK * 2) + 16 * src_col + 4096 - 1024 * (j0 - 2);
     }
-#pragma unroll
-    for (int j0 = 0; j0 < NJ; ++j0) {
-      const int j = j0 * NW + wave;
-      if (j < S::DMA_BLOCKS) {
-        const int p = 64 * j + ln;
-        const int r = p / S::PPR, pp = p % S::PPR;
-        const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
-        const int src_col = lp < S::RPR ? lp : lp - S::RPR;  // pad pieces meet zero q
-        // row indices are < 2^24 (one sequence's cache is < 4 GiB)
-        dma16(__builtin_amdgcn_readfirstlane(lds_offset(dst + 1024 * j)), kv_seq,
-              __umul24((uint32_t)max(idx[j0], 0), DQK * 2) + 16 * src_col);
-      }
-    }
+    const uint32_t mid =
+        __builtin_amdgcn_readfirstlane(lds_offset(kvb + buf * S::CHUNK_BYTES + 1024 * (j_lo + 2)));
+    if (long_run) dma_run<NJ>(mid, kv_bias, off);
+    else dma_run<NJ - 1>(mid, kv_bias, off);
   };
 
   // physical byte offset of logical 16-byte piece `lp` in LDS row `r`
@@ -235,8 +264,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
 
     // wait for this chunk's gather: at most one later chunk is in flight here
     if (it + 1 < total) {
-      if (wave < S::DMA_HI_WAVES) wait_vmcnt<S::DMA_LO + 1>();
-      else wait_vmcnt<S::DMA_LO>();
+      if (long_run) wait_vmcnt<NJ>();
+      else wait_vmcnt<NJ - 1>();
     } else {
       wait_vmcnt<0>();
     }
