@@ -6,12 +6,13 @@
 // section "How the lightning indexer works"; DeepSeek-V3.2 spec sheet, section
 // 2.1).  Ties at the threshold go to the lower index; output is ascending.
 //
-// Scores are mapped to order-preserving 32-bit keys (-0 folded onto +0).  Up to
-// three digit passes (11, 11 and 10 bits) build LDS histograms of the keys that
-// still match the chosen prefix and pick the digit holding the k-th largest
-// key.  A pass stops early when every key of the chosen bin is selected.  The
-// ordered compaction then keeps, in index order, the keys above the threshold
-// and the first (needed) keys equal to it.
+// Scores are mapped to order-preserving 32-bit keys (-0 folded onto +0).  Digit
+// passes build LDS histograms of the keys that still match the chosen prefix
+// and pick the digit holding the k-th largest key; a pass stops early when
+// every key of the chosen bin is selected.  The ordered compaction then keeps,
+// in index order, the keys above the threshold and the first (needed) keys
+// equal to it.  Rows held in registers are first cut down to a few thousand
+// candidates with a threshold taken from a sample (see select_top).
 //  * Rows of up to 32768 candidates: one block, keys held in registers.
 //  * Longer rows: two stages through a workspace (per-segment top k, then the
 //    top k of the segments' candidates), which also spreads a few long rows
@@ -34,57 +35,156 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Inclusive block scan of v over kThreads threads; `sh` holds kWaves+1 words.
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) sh[wave] = v;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t x = lane < kWaves ? sh[lane] : 0u;
-#pragma unroll
-    for (int o = 1; o < kWaves; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane < kWaves) sh[lane] = x;
-  }
-  __syncthreads();
-  const uint32_t add = wave > 0 ? sh[wave - 1] : 0u;
-  total = sh[kWaves - 1];
-  __syncthreads();
-  return v + add;
+// Wave-wide inclusive scans through DPP row shifts and row broadcasts (VALU
+// only; a shuffle would be an LDS-crossbar round trip per step).  `id` is the
+// identity of `op`; lane 63 ends up with the wave total.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op) {
+  auto dpp = [&](uint32_t v, auto ctrl, auto rows) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, decltype(ctrl)::value,
+                                                 decltype(rows)::value, 0xf, false);
+  };
+  x = op(x, dpp(x, std::integral_constant<int, 0x111>(), std::integral_constant<int, 0xf>()));  // row_shr:1
+  x = op(x, dpp(x, std::integral_constant<int, 0x112>(), std::integral_constant<int, 0xf>()));  // row_shr:2
+  x = op(x, dpp(x, std::integral_constant<int, 0x114>(), std::integral_constant<int, 0xf>()));  // row_shr:4
+  x = op(x, dpp(x, std::integral_constant<int, 0x118>(), std::integral_constant<int, 0xf>()));  // row_shr:8
+  x = op(x, dpp(x, std::integral_constant<int, 0x142>(), std::integral_constant<int, 0xa>()));  // row_bcast:15
+  x = op(x, dpp(x, std::integral_constant<int, 0x143>(), std::integral_constant<int, 0xc>()));  // row_bcast:31
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_scan_add(uint32_t x) {
+  return wave_scan(x, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 
+// Inclusive block scan of v over NT threads; `sh` holds NT/64 words.
 template <int NT>
 __device__ __forceinline__ uint32_t block_inclusive_scan_n(uint32_t v, uint32_t* sh, uint32_t& total) {
   constexpr int NWV = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  v = wave_scan_add(v);
   if (lane == 63) sh[wave] = v;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t x = lane < NWV ? sh[lane] : 0u;
+  uint32_t add = 0, tot = 0;
 #pragma unroll
-    for (int o = 1; o < NWV; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    if (lane < NWV) sh[lane] = x;
+  for (int w = 0; w < NWV; ++w) {
+    const uint32_t s = sh[w];
+    add += w < wave ? s : 0u;
+    tot += s;
   }
-  __syncthreads();
-  const uint32_t add = wave > 0 ? sh[wave - 1] : 0u;
-  total = sh[NWV - 1];
+  total = tot;
   __syncthreads();
   return v + add;
+}
+
+// Block-wide min of lo and max of hi over NT threads (results in every
+// thread); `sh` holds at least 2 * NT / 64 words.
+template <int NT>
+__device__ __forceinline__ void block_minmax(uint32_t& lo, uint32_t& hi, uint32_t* sh) {
+  constexpr int NWV = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  lo = wave_scan(lo, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); });
+  hi = wave_scan(hi, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+  if (lane == 63) {
+    sh[wave] = lo;
+    sh[NWV + wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NWV; ++w) {
+    lo = min(lo, sh[w]);
+    hi = max(hi, sh[NWV + w]);
+  }
+  __syncthreads();
+}
+
+// Selection among n candidates whose keys are re-read through key_at(i) on
+// every pass (global memory, mostly L2): fixed digits of 11, 11 and 10 bits
+// from the top of the key, no register array.  emit(o, c, key) as below.
+template <int NT, typename KeyAt, typename Emit>
+__device__ __forceinline__ void select_streamed(uint32_t* hist, uint32_t* scan_sh, uint32_t* ctrl,
+                                                KeyAt&& key_at, int n, uint32_t k, Emit&& emit) {
+  constexpr int BPT = kBins / NT;
+  uint32_t prefix = 0, mask = 0;
+  uint32_t need = k;  // keys still to take among those matching prefix
+  bool all_ge = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint32_t key = key_at(i);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // thread i owns bins kBins-1-BPT*i down to kBins-BPT*(i+1); an inclusive
+    // scan in descending bin order gives suffix counts.  The chosen digit d
+    // satisfies count(>= d) >= need > count(> d).
+    uint32_t h[BPT], hs = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      h[e] = hist[kBins - 1 - BPT * (int)threadIdx.x - e];
+      hs += h[e];
+    }
+    uint32_t total;
+    uint32_t above = block_inclusive_scan_n<NT>(hs, scan_sh, total) - hs;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      if (above < need && need <= above + h[e]) {
+        ctrl[0] = (uint32_t)(kBins - 1 - BPT * (int)threadIdx.x - e);
+        ctrl[1] = above;
+      }
+      above += h[e];
+    }
+    __syncthreads();
+    const uint32_t d = ctrl[0];
+    need -= ctrl[1];
+    prefix |= d << shift;
+    mask |= dmask << shift;
+    const uint32_t bin_count = hist[d];
+    __syncthreads();
+    if (bin_count == need) { all_ge = true; break; }
+  }
+
+  // ---- ordered compaction, 4 * NT candidates at a time
+  const uint32_t T = prefix;
+  uint32_t gt_base = 0, eq_base = 0;
+  for (int base = 0; base < n; base += 4 * NT) {
+    const int i0 = base + 4 * threadIdx.x;
+    uint32_t keys[4];
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j;
+      const bool in = i < n;
+      keys[j] = in ? key_at(i) : 0u;
+      gt += in && (all_ge ? keys[j] >= T : keys[j] > T);
+      eq += in && !all_ge && keys[j] == T;
+    }
+    uint32_t total;
+    const uint32_t packed = gt | (eq << 16);
+    const uint32_t excl = block_inclusive_scan_n<NT>(packed, scan_sh, total) - packed;
+    uint32_t gt_before = gt_base + (excl & 0xFFFFu);
+    uint32_t eq_before = eq_base + (excl >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j;
+      if (i >= n) break;
+      const bool is_gt = all_ge ? keys[j] >= T : keys[j] > T;
+      const bool is_eq = !all_ge && keys[j] == T;
+      if (is_gt) {
+        const uint32_t o = gt_before + min(eq_before, need);
+        if (o < k) emit(o, i, keys[j]);
+        ++gt_before;
+      } else if (is_eq) {
+        if (eq_before < need && gt_before + eq_before < k) emit(gt_before + eq_before, i, keys[j]);
+        ++eq_before;
+      }
+    }
+    gt_base += total & 0xFFFFu;
+    eq_base += total >> 16;
+  }
 }
 
 // Fallback for rows too long for the two-stage path: the row is re-read from
@@ -106,146 +206,165 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
     return;
   }
   const float* srow = a.scores + (size_t)row * a.Lk;
-
-  uint32_t prefix = 0, mask = 0;
-  uint32_t need = (uint32_t)a.k;  // keys still to take among those matching prefix
-  bool all_ge = false;
-
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
-    __syncthreads();
-    for (int i = threadIdx.x; i < n; i += kThreads) {
-      const uint32_t key = order_key(srow[i]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // Thread i owns bins (2047-2i, 2046-2i); an inclusive scan in descending bin
-    // order gives suffix counts.  The chosen digit d satisfies
-    // count(>= d) >= need > count(> d).
-    const int b0 = kBins - 1 - 2 * (int)threadIdx.x, b1 = b0 - 1;
-    const uint32_t h0 = hist[b0], h1 = hist[b1];
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan(h0 + h1, scan_sh, total);
-    const uint32_t excl = incl - h0 - h1;
-    if (excl < need && need <= excl + h0) { ctrl[0] = (uint32_t)b0; ctrl[1] = excl; }
-    if (excl + h0 < need && need <= incl) { ctrl[0] = (uint32_t)b1; ctrl[1] = excl + h0; }
-    __syncthreads();
-    const uint32_t d = ctrl[0];
-    need -= ctrl[1];
-    prefix |= d << shift;
-    mask |= dmask << shift;
-    const uint32_t bin_count = hist[d];
-    __syncthreads();
-    if (bin_count == need) { all_ge = true; break; }
-  }
-
-  // ---- ordered compaction
-  const uint32_t T = prefix;
-  uint32_t gt_base = 0, eq_base = 0;
-  for (int base = 0; base < n; base += 4 * kThreads) {
-    const int i0 = base + 4 * threadIdx.x;
-    uint32_t keys[4];
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j;
-      keys[j] = i < n ? order_key(srow[i]) : 0u;
-      const bool in = i < n;
-      const bool is_gt = in && (all_ge ? keys[j] >= T : keys[j] > T);
-      const bool is_eq = in && !all_ge && keys[j] == T;
-      gt += is_gt; eq += is_eq;
-    }
-    uint32_t total;
-    const uint32_t incl = block_inclusive_scan(gt | (eq << 16), scan_sh, total);
-    const uint32_t excl = incl - (gt | (eq << 16));
-    uint32_t gt_before = gt_base + (excl & 0xFFFFu);
-    uint32_t eq_before = eq_base + (excl >> 16);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = i0 + j;
-      if (i >= n) break;
-      const bool is_gt = all_ge ? keys[j] >= T : keys[j] > T;
-      const bool is_eq = !all_ge && keys[j] == T;
-      if (is_gt) {
-        const uint32_t o = gt_before + min(eq_before, need);
-        if (o < (uint32_t)a.k) out[o] = i;
-        ++gt_before;
-      } else if (is_eq) {
-        if (eq_before < need && gt_before + eq_before < (uint32_t)a.k) out[gt_before + eq_before] = i;
-        ++eq_before;
-      }
-    }
-    gt_base += total & 0xFFFFu;
-    eq_base += total >> 16;
-  }
+  select_streamed<kThreads>(hist, scan_sh, ctrl, [&](int i) { return order_key(srow[i]); }, n,
+                            (uint32_t)a.k, [&](uint32_t o, int c, uint32_t) { out[o] = c; });
 }
 
-// Register-resident selection among n <= EPT * NT candidates c = 0..n-1:
-// thread t holds the keys of the contiguous candidates [EPT*t, EPT*t + EPT), so
-// the digit passes touch LDS only for the histogram and the ordered compaction
-// needs a single block-wide scan.  Key 0 marks an absent candidate (real keys
-// are >= 1 where absent ones can occur).  emit(o, c, key) is called for the k
-// selected candidates, o = their rank in ascending c.
-template <int EPT, int NT>
-struct RegSelect {
-  static constexpr int BPT = kBins / NT;  // histogram bins per thread in the digit scan
+// Block-wide selection among n candidates c = 0..n-1 held in registers:
+// thread t holds the keys of the contiguous candidates [EPT*t, EPT*t + EPT).
+// Key 0 marks an absent candidate (real keys are >= 1 where absent ones can
+// occur).  emit(o, c, key) is called for the k selected candidates, o = their
+// rank in ascending c.
+//
+// Radix passes over all n keys cost one LDS atomic per key and pass, random
+// histogram updates conflict in the LDS banks, and every pass is a chain of
+// barriers, so long rows are first cut down: one histogram pass over a
+// stride-16 sample gives a bin edge t with about r sampled keys above it (r a
+// few standard deviations above the expected sampled rank of the k-th key),
+// the keys >= t are counted, and when there are between k and kCap of them
+// they are compacted, in index order, into LDS, where the exact selection
+// runs.  This is exact: at least k keys >= t means the k-th largest key is
+// >= t, so every key that can be selected, ties included, is a candidate, and
+// the candidates keep their index order.  Otherwise the passes run on all keys.
+constexpr int kCap = 4096;     // LDS candidate slots
+constexpr int kDigit = 12;     // bits per radix digit
+constexpr int kHist = 1 << kDigit;
+
+template <int NT>
+struct BlockSelect {
+  static constexpr int BPT = kHist / NT;  // histogram bins per thread in the digit scan
   uint32_t* hist;
   uint32_t* scan_sh;
   uint32_t* ctrl;
 
-  template <typename Emit>
-  __device__ __forceinline__ void run(const uint32_t (&key)[EPT], int cnt, int base, uint32_t k,
-                                      Emit&& emit) {
-    uint32_t prefix = 0, mask = 0;
-    uint32_t need = k;
-    bool all_ge = false;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-      for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < EPT; ++j)
-        if (j < cnt && (key[j] & mask) == prefix) atomicAdd(&hist[(key[j] >> shift) & dmask], 1u);
-      __syncthreads();
-      // thread i owns bins kBins-1-BPT*i down to kBins-BPT*(i+1); a scan in
-      // descending bin order gives suffix counts
-      uint32_t h[BPT], hs = 0;
-#pragma unroll
-      for (int e = 0; e < BPT; ++e) {
-        h[e] = hist[kBins - 1 - BPT * (int)threadIdx.x - e];
-        hs += h[e];
-      }
-      uint32_t total;
-      const uint32_t incl = block_inclusive_scan_n<NT>(hs, scan_sh, total);
-      uint32_t above = incl - hs;
-#pragma unroll
-      for (int e = 0; e < BPT; ++e) {
-        if (above < need && need <= above + h[e]) {
-          ctrl[0] = (uint32_t)(kBins - 1 - BPT * (int)threadIdx.x - e);
-          ctrl[1] = above;
-        }
-        above += h[e];
-      }
-      __syncthreads();
-      const uint32_t d = ctrl[0];
-      need -= ctrl[1];
-      prefix |= d << shift;
-      mask |= dmask << shift;
-      const uint32_t bin_count = hist[d];
-      __syncthreads();
-      if (bin_count == need) { all_ge = true; break; }
-    }
+  __device__ __forceinline__ uint32_t sum(uint32_t v) {
+    uint32_t total;
+    block_inclusive_scan_n<NT>(v, scan_sh, total);
+    return total;
+  }
 
-    // ---- ordered compaction: one scan of per-thread (greater, equal) counts
-    const uint32_t T = prefix;
+  // One digit pass: histogram of the digit (r >> shift) & dmask of the keys
+  // key[j < cnt] with r >> cur == pref (r = key - kmin; every key when cur is
+  // 32), then the digit holding the need-th largest of them.  Returns the
+  // digit; `above` = the matching keys in higher digits, `in_bin` = in it.
+  template <int E>
+  __device__ __forceinline__ uint32_t digit_pass(const uint32_t (&key)[E], int cnt, uint32_t kmin, int cur,
+                                                 uint32_t pref, int shift, uint32_t dmask, uint32_t need,
+                                                 uint32_t& above_out, uint32_t& in_bin) {
+    for (int i = threadIdx.x; i < kHist; i += NT) hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint32_t r = key[j] - kmin;
+      const bool match = cur >= 32 || (r >> cur) == pref;
+      if (j < cnt && match) atomicAdd(&hist[(r >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    // thread i owns bins kHist-1-BPT*i down to kHist-BPT*(i+1); a scan in
+    // descending bin order gives suffix counts
+    uint32_t h[BPT], hs = 0;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      h[e] = hist[kHist - 1 - BPT * (int)threadIdx.x - e];
+      hs += h[e];
+    }
+    uint32_t total;
+    const uint32_t incl = block_inclusive_scan_n<NT>(hs, scan_sh, total);
+    uint32_t above = incl - hs;
+#pragma unroll
+    for (int e = 0; e < BPT; ++e) {
+      if (above < need && need <= above + h[e]) {
+        ctrl[0] = (uint32_t)(kHist - 1 - BPT * (int)threadIdx.x - e);
+        ctrl[1] = above;
+        ctrl[2] = h[e];
+      }
+      above += h[e];
+    }
+    __syncthreads();
+    const uint32_t dg = ctrl[0];
+    above_out = ctrl[1];
+    in_bin = ctrl[2];
+    __syncthreads();
+    return dg;
+  }
+
+  // min and max of the keys key[j < cnt] of the block
+  template <int E>
+  __device__ __forceinline__ void range(const uint32_t (&key)[E], int cnt, uint32_t& lo, uint32_t& hi) {
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (j < cnt) {
+        lo = min(lo, key[j]);
+        hi = max(hi, key[j]);
+      }
+    block_minmax<NT>(lo, hi, scan_sh);
+  }
+
+  // A key value t such that at least k (1 <= k <= their number) of the keys
+  // are >= t: the lower edge of the top digit bin that reaches k.
+  template <int E>
+  __device__ __forceinline__ uint32_t coarse_threshold(const uint32_t (&key)[E], int cnt, uint32_t k) {
+    uint32_t lo, hi;
+    range(key, cnt, lo, hi);
+    const int cur = hi > lo ? 32 - __builtin_clz(hi - lo) : 0;
+    if (cur == 0) return lo;
+    const int d = min(kDigit, cur);
+    uint32_t above, in_bin;
+    const uint32_t dg = digit_pass(key, cnt, lo, 32, 0u, cur - d, (1u << d) - 1u, k, above, in_bin);
+    return lo + (dg << (cur - d));
+  }
+
+  // Threshold of the k-th largest of the keys key[j < cnt] of the block
+  // (1 <= k <= their number): the selected keys are those > T plus the first
+  // `need` (in candidate order) equal to T, or all keys >= T when all_ge.
+  // The keys are left rebased by kmin (and T is too): restoring them would
+  // make the compiler keep the original keys alive as a second copy.
+  // The digits are taken from r = key - kmin, starting at the top bit of
+  // kmax - kmin: the keys of one row span a few binades, so digits cut from the
+  // top of the raw key would crowd them into a handful of bins.
+  template <int E>
+  __device__ __forceinline__ void threshold(uint32_t (&key)[E], int cnt, uint32_t k, uint32_t& T,
+                                            uint32_t& need, bool& all_ge, uint32_t& kmin) {
+    uint32_t lo, hi;
+    range(key, cnt, lo, hi);
+    kmin = lo;
+    // Rebased in place, through asm so that each key keeps its register: key -
+    // lo recomputed in every pass is hoisted out of the pass loop, and a plain
+    // subtraction is given fresh registers while the originals are still live
+    // (either way a second copy of the keys).
+    const uint32_t lo_s = __builtin_amdgcn_readfirstlane(lo);
+#pragma unroll
+    for (int j = 0; j < E; ++j) asm volatile("v_subrev_u32 %0, %1, %0" : "+v"(key[j]) : "s"(lo_s));
+    int cur = hi > lo ? 32 - __builtin_clz(hi - lo) : 0;  // bits of r still undecided
+    uint32_t pref = 0;                                     // r >> cur of the chosen keys
+    need = k;
+    all_ge = false;
+#pragma unroll 1
+    while (cur > 0) {
+      const int d = min(kDigit, cur);
+      const int shift = cur - d;
+      uint32_t above, in_bin;
+      const uint32_t dg = digit_pass(key, cnt, 0u, cur, pref, shift, (1u << d) - 1u, need, above, in_bin);
+      need -= above;
+      pref = (pref << d) | dg;
+      cur = shift;
+      if (in_bin == need) { all_ge = true; break; }
+    }
+    T = pref << cur;  // cur < 32 here: a range of 32 bits takes a pass
+  }
+
+  // Ordered emission of the keys chosen by threshold() (keys and T rebased
+  // by kmin): one scan of the per-thread (greater, equal) counts gives every
+  // key its output rank.
+  template <int E, typename Emit>
+  __device__ __forceinline__ void emit_top(const uint32_t (&key)[E], int cnt, int base, uint32_t k,
+                                           uint32_t T, uint32_t need, bool all_ge, uint32_t kmin,
+                                           Emit&& emit) {
     uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
+    for (int j = 0; j < E; ++j) {
       if (j < cnt) {
         gt += all_ge ? key[j] >= T : key[j] > T;
         eq += !all_ge && key[j] == T;
@@ -256,22 +375,84 @@ struct RegSelect {
     const uint32_t excl = block_inclusive_scan_n<NT>(packed, scan_sh, total) - packed;
     uint32_t gt_before = excl & 0xFFFFu, eq_before = excl >> 16;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
+    for (int j = 0; j < E; ++j) {
       if (j < cnt) {
         const bool is_gt = all_ge ? key[j] >= T : key[j] > T;
         const bool is_eq = !all_ge && key[j] == T;
         if (is_gt) {
           const uint32_t o = gt_before + min(eq_before, need);
-          if (o < k) emit(o, base + j, key[j]);
+          if (o < k) emit(o, base + j, key[j] + kmin);
           ++gt_before;
         } else if (is_eq) {
-          if (eq_before < need && gt_before + eq_before < k) emit(gt_before + eq_before, base + j, key[j]);
+          if (eq_before < need && gt_before + eq_before < k)
+            emit(gt_before + eq_before, base + j, key[j] + kmin);
           ++eq_before;
         }
       }
     }
   }
 };
+
+// The k largest of the n (> k) candidates held as described above; `ck` and
+// `ci` are kCap-slot LDS arrays.
+template <int EPT, int NT, typename KeyAt, typename Emit>
+__device__ __forceinline__ void select_top(BlockSelect<NT> sel, uint32_t (&key)[EPT], int cnt, int n,
+                                           uint32_t k, uint32_t* ck, int32_t* ci, KeyAt&& key_at,
+                                           Emit&& emit) {
+  static_assert(EPT % 16 == 0 && kCap % NT == 0, "sample stride and candidate slots");
+  constexpr int S = EPT / 16;     // samples per thread: candidates 16s of its range
+  constexpr int E2 = kCap / NT;   // candidates per thread in the exact selection
+  const int base = EPT * (int)threadIdx.x;
+  uint32_t t = 0;  // every key is >= 0
+  bool filtered = true;
+  if (n > kCap) {
+    uint32_t smp[S];
+#pragma unroll
+    for (int e = 0; e < S; ++e) smp[e] = key[16 * e];
+    const int scnt = min(S, (cnt + 15) / 16);
+    const uint32_t m = (uint32_t)(n + 15) / 16;  // sampled candidates: 0, 16, 32, ... < n
+    const float qm = (float)k * (float)m / (float)n;
+    const uint32_t r = min(m, (uint32_t)(qm + 4.0f * sqrtf(qm) + 8.0f));
+    t = sel.coarse_threshold(smp, scnt, r);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) c += j < cnt && key[j] >= t;
+    c = sel.sum(c);
+    filtered = c >= k && c <= (uint32_t)kCap;
+  }
+  if (filtered) {
+    // recomputed below rather than kept from the count: 64 live predicates
+    // would cost as many registers as the keys
+    asm volatile("" : "+v"(t));
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) mine += j < cnt && key[j] >= t;
+    uint32_t total;
+    uint32_t o = block_inclusive_scan_n<NT>(mine, sel.scan_sh, total) - mine;
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (j < cnt && key[j] >= t) {
+        ck[o] = key[j];
+        ci[o] = base + j;
+        ++o;
+      }
+    __syncthreads();
+    const int b2 = E2 * (int)threadIdx.x;
+    const int cnt2 = max(0, min(E2, (int)total - b2));
+    uint32_t k2[E2];
+#pragma unroll
+    for (int e = 0; e < E2; ++e) k2[e] = e < cnt2 ? ck[b2 + e] : 0u;
+    uint32_t T, need, kmin;
+    bool all_ge;
+    sel.threshold(k2, cnt2, k, T, need, all_ge, kmin);
+    sel.emit_top(k2, cnt2, b2, k, T, need, all_ge, kmin,
+                 [&](uint32_t o2, int c2, uint32_t kv) { emit(o2, ci[c2], kv); });
+  } else {
+    // the registers are not used here: a second register-array selection
+    // would double the kernel's register count for a rare case
+    select_streamed<NT>(sel.hist, sel.scan_sh, sel.ctrl, key_at, n, k, emit);
+  }
+}
 
 // Keys of the scores [base, base + cnt) of one row; VEC: 16-byte loads.
 template <int EPT, bool VEC>
@@ -292,9 +473,11 @@ __device__ __forceinline__ void load_keys(const float* src, int base, int cnt, u
 // One block per row of at most EPT * NT candidates.
 template <int EPT, bool VEC, int NT>
 __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t scan_sh[NT / 64 + 1];
+  __shared__ uint32_t hist[kHist];
+  __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
   __shared__ uint32_t ctrl[4];
+  __shared__ uint32_t cand_k[kCap];
+  __shared__ int32_t cand_i[kCap];
   const int row = blockIdx.x;
   const int pos = a.q_start + row % a.Lq;
   const int n = min(pos + 1, a.Lk);
@@ -307,8 +490,10 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
   const int cnt = max(0, min(EPT, n - base));
   uint32_t key[EPT];
   load_keys<EPT, VEC>(a.scores + (size_t)row * a.Lk, base, cnt, key);
-  RegSelect<EPT, NT>{hist, scan_sh, ctrl}.run(key, cnt, base, (uint32_t)a.k,
-                                              [&](uint32_t o, int c, uint32_t) { out[o] = c; });
+  const float* srow = a.scores + (size_t)row * a.Lk;
+  select_top<EPT, NT>(BlockSelect<NT>{hist, scan_sh, ctrl}, key, cnt, n, (uint32_t)a.k, cand_k, cand_i,
+                      [&](int i) { return order_key(srow[i]); },
+                      [&](uint32_t o, int c, uint32_t) { out[o] = c; });
 }
 
 // Rows longer than one block holds are selected in two stages.  The top k of
@@ -328,9 +513,11 @@ constexpr int kCandMax = 64 * 512;  // candidates per row that stage 2 can hold
 template <bool VEC>
 __global__ __launch_bounds__(kSegNT) void topk_seg_kernel(TopkArgs a) {
   constexpr int EPT = kSeg / kSegNT;
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t scan_sh[kSegNT / 64 + 1];
+  __shared__ uint32_t hist[kHist];
+  __shared__ uint32_t scan_sh[2 * (kSegNT / 64) + 1];
   __shared__ uint32_t ctrl[4];
+  __shared__ uint32_t cand_k[kCap];
+  __shared__ int32_t cand_i[kCap];
   const int row = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
   const int pos = a.q_start + row % a.Lq;
@@ -352,19 +539,22 @@ __global__ __launch_bounds__(kSegNT) void topk_seg_kernel(TopkArgs a) {
   const int cnt = max(0, min(EPT, n - base));
   uint32_t key[EPT];
   load_keys<EPT, VEC>(src, base, cnt, key);
-  RegSelect<EPT, kSegNT>{hist, scan_sh, ctrl}.run(key, cnt, base, (uint32_t)a.k,
-                                                  [&](uint32_t o, int c, uint32_t kv) {
-                                                    ck[o] = max(kv, 1u);
-                                                    ci[o] = s0 + c;
-                                                  });
+  select_top<EPT, kSegNT>(BlockSelect<kSegNT>{hist, scan_sh, ctrl}, key, cnt, n, (uint32_t)a.k, cand_k,
+                          cand_i, [&](int i) { return order_key(src[i]); },
+                          [&](uint32_t o, int c, uint32_t kv) {
+                            ck[o] = max(kv, 1u);
+                            ci[o] = s0 + c;
+                          });
 }
 
 // Stage 2: one block per row selects among its nseg * k candidate slots.
 __global__ __launch_bounds__(512) void topk_cand_kernel(TopkArgs a) {
   constexpr int NT = 512, EPT = kCandMax / NT;
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t scan_sh[NT / 64 + 1];
+  __shared__ uint32_t hist[kHist];
+  __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
   __shared__ uint32_t ctrl[4];
+  __shared__ uint32_t cand_k[kCap];
+  __shared__ int32_t cand_i[kCap];
   const int row = blockIdx.x;
   const int pos = a.q_start + row % a.Lq;
   const int n_row = min(pos + 1, a.Lk);
@@ -390,8 +580,9 @@ __global__ __launch_bounds__(512) void topk_cand_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < EPT; ++j) key[j] = j < cnt ? ck[base + j] : 0u;
   }
-  RegSelect<EPT, NT>{hist, scan_sh, ctrl}.run(key, cnt, base, (uint32_t)a.k,
-                                              [&](uint32_t o, int c, uint32_t) { out[o] = ci[c]; });
+  select_top<EPT, NT>(BlockSelect<NT>{hist, scan_sh, ctrl}, key, cnt, n, (uint32_t)a.k, cand_k, cand_i,
+                      [&](int i) { return ck[i]; },
+                      [&](uint32_t o, int c, uint32_t) { out[o] = ci[c]; });
 }
 
 // Segments per row for the two-stage path (0: the row fits one block or the
