@@ -127,15 +127,21 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   __builtin_assume(wave >= 0 && wave < NW);
   const int g = lane >> 4;
   const int li = lane & 15;
-  const int row = blockIdx.x / a.nsplit;
-  const int part = blockIdx.x % a.nsplit;
+  // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8), each
+  // with its own L2.  Neighbouring query rows select largely the same latent
+  // rows, so each XCD takes a contiguous range of (row, part) items instead
+  // of every 8th one, and their gathers meet in the same L2.
+  const int nb = gridDim.x;
+  const int vb = (blockIdx.x & 7) * (nb >> 3) + min((int)(blockIdx.x & 7), nb & 7) + (blockIdx.x >> 3);
+  const int row = vb / a.nsplit;
+  const int part = vb % a.nsplit;
   const int b = row / a.Lq;
   const int nch = (a.k + kChunk - 1) / kChunk;
   // chunks [c_lo, c_hi) of the row belong to this block
   const int c_lo = part * nch / a.nsplit, c_hi = (part + 1) * nch / a.nsplit;
-  float* out_base = a.nsplit > 1 ? a.part_out + (size_t)blockIdx.x * a.H * DV
+  float* out_base = a.nsplit > 1 ? a.part_out + (size_t)vb * a.H * DV
                                  : a.out + (size_t)row * a.H * DV;
-  float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)blockIdx.x * a.H
+  float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)vb * a.H
                                  : (a.lse ? a.lse + (size_t)row * a.H : nullptr);
 
   // ---- selected indices -> LDS (entries outside [0, Lk) become -1)
