@@ -129,10 +129,17 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   const int li = lane & 15;
   // Workgroups are dealt to the 8 XCDs in turn (block b to XCD b % 8), each
   // with its own L2.  Neighbouring query rows select largely the same latent
-  // rows, so each XCD takes a contiguous range of (row, part) items instead
-  // of every 8th one, and their gathers meet in the same L2.
+  // rows, so (row, part) items go to the XCDs in runs of kXcdRun consecutive
+  // ones instead of one at a time, and their gathers meet in the same L2;
+  // runs rather than one range per XCD keep the causal rows' uneven work
+  // spread over all XCDs.  Blocks past the last whole round keep their index.
+  constexpr int kXcdRun = 16;
   const int nb = gridDim.x;
-  const int vb = (blockIdx.x & 7) * (nb >> 3) + min((int)(blockIdx.x & 7), nb & 7) + (blockIdx.x >> 3);
+  const int full = nb / (8 * kXcdRun) * (8 * kXcdRun);
+  const int xi = blockIdx.x >> 3;
+  const int vb = (int)blockIdx.x < full
+                     ? ((xi / kXcdRun) * 8 + (int)(blockIdx.x & 7)) * kXcdRun + xi % kXcdRun
+                     : (int)blockIdx.x;
   const int row = vb / a.nsplit;
   const int part = vb % a.nsplit;
   const int b = row / a.Lq;
