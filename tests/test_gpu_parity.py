@@ -108,6 +108,38 @@ def test_topk_ties_and_signed_zero(dsa):
     np.testing.assert_array_equal(idx.cpu().numpy().reshape(Lq, k), ref)
 
 
+@pytest.mark.parametrize("k", [2048, 64])
+def test_topk_sampled_threshold_paths(dsa, k):
+    """Rows of up to 32K candidates are first cut down with a threshold taken
+    from a stride-16 sample; these rows drive every outcome of that step: the
+    normal case, a sample that overshoots (fewer than k keys clear the
+    threshold), one that undershoots (more keys than the candidate buffer),
+    an all-equal row and heavy ties, each against the oracle."""
+    rng = np.random.default_rng(11 + k)
+    B, Lq, Lk = 1, 8, 20000
+    q_start = Lk - Lq
+    wl = dsa_inputs.Workload("sampled", 0, B, Lq, Lk, q_start, 4, 32, k, 8, 64, 16)
+    s = rng.standard_normal((B, Lq, Lk)).astype(np.float32)       # row 0: normal path
+    comb = (np.arange(Lk) % 16) == 0
+    s[0, 1] = np.where(comb, 5.0 + rng.random(Lk), rng.random(Lk)).astype(np.float32)   # sample overshoots
+    s[0, 2] = np.where(comb, rng.random(Lk), 5.0 + rng.random(Lk)).astype(np.float32)   # sample undershoots
+    s[0, 3] = 1.5                                                   # all equal
+    s[0, 4] = rng.integers(0, 3, Lk).astype(np.float32)            # three values, heavy ties
+    s[0, 5] = (rng.integers(-20, 21, Lk) * 0.125).astype(np.float32)  # quantised
+    s[0, 6, :] = -0.0                                               # signed zeros with a few spikes
+    s[0, 6, rng.choice(Lk, 50, replace=False)] = 0.0
+    s[0, 6, rng.choice(Lk, 30, replace=False)] = 2.0
+    prob = dsa.Problem.from_workload(wl)
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Lq, k), dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(prob, dev(s), idx, ws, ws_bytes)
+    torch.cuda.synchronize()
+    pos = (q_start + np.arange(Lq)).astype(np.int32)
+    ref = oracle.topk(np.ascontiguousarray(s[0]), pos, k)
+    np.testing.assert_array_equal(idx.cpu().numpy()[0], ref)
+
+
 @pytest.mark.parametrize("k,Lk,Lq", [(64, 40000, 6), (2048, 40000, 4), (100, 65536, 3)])
 def test_topk_two_stage_long_rows(dsa, k, Lk, Lq):
     """Rows longer than one block holds go through per-segment selection and a
