@@ -83,6 +83,9 @@ WORKLOADS: Dict[str, Workload] = {
     "prefill32k": Workload("prefill32k", 2, 1, 32768, 32768, 0, 64, 128, 2048, 128, 512, 64),
     "decode": Workload("decode", 3, 64, 1, 131072, 131071, 64, 128, 2048, 128, 512, 64),
     "chunked": Workload("chunked", 4, 1, 8192, 131072, 122880, 64, 128, 2048, 128, 512, 64),
+    # 1M-token contexts (the indexer's surviving quadratic term at long context)
+    "decode1m": Workload("decode1m", 5, 4, 1, 1048576, 1048575, 64, 128, 2048, 128, 512, 64),
+    "chunked1m": Workload("chunked1m", 6, 1, 4096, 1048576, 1044480, 64, 128, 2048, 128, 512, 64),
 }
 
 

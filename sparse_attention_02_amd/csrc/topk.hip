@@ -506,13 +506,18 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
 // min(k, length) candidates as (key, index) into slots [row][segment][0..k),
 // in ascending index order; unused slots hold key 0 and index -1.  Real keys
 // are made >= 1 so that a padding slot never ties with a candidate.
+// Rows that the 512-thread stage 2 can merge use segments of kSeg keys (256
+// threads x 32); longer rows (up to 1M candidates at k = 2048) use segments
+// of kSegWide keys (512 threads x 64) and a 1024-thread stage 2.
 constexpr int kSeg = 8192;
-constexpr int kSegNT = 256;
-constexpr int kCandMax = 64 * 512;  // candidates per row that stage 2 can hold
+constexpr int kSegWide = 32768;
+constexpr int kCandMax = 64 * 512;    // candidates per row that stage 2 can hold
+constexpr int kCandWide = 64 * 1024;  // ... the wide stage 2
 
-template <bool VEC>
-__global__ __launch_bounds__(kSegNT) void topk_seg_kernel(TopkArgs a) {
-  constexpr int EPT = kSeg / kSegNT;
+template <int EPT, int NT, bool VEC>
+__global__ __launch_bounds__(NT) void topk_seg_kernel(TopkArgs a) {
+  constexpr int kSegLen = EPT * NT;
+  constexpr int kSegNT = NT;
   __shared__ uint32_t hist[kHist];
   __shared__ uint32_t scan_sh[2 * (kSegNT / 64) + 1];
   __shared__ uint32_t ctrl[4];
@@ -523,8 +528,8 @@ __global__ __launch_bounds__(kSegNT) void topk_seg_kernel(TopkArgs a) {
   const int pos = a.q_start + row % a.Lq;
   const int n_row = min(pos + 1, a.Lk);
   if (n_row <= a.k) return;  // stage 2 writes short rows directly
-  const int s0 = seg * kSeg;
-  const int n = max(0, min(kSeg, n_row - s0));
+  const int s0 = seg * kSegLen;
+  const int n = max(0, min(kSegLen, n_row - s0));
   uint32_t* ck = a.cand_key + ((size_t)row * a.nseg + seg) * a.k;
   int32_t* ci = a.cand_idx + ((size_t)row * a.nseg + seg) * a.k;
   const float* src = a.scores + (size_t)row * a.Lk + s0;
@@ -547,9 +552,10 @@ __global__ __launch_bounds__(kSegNT) void topk_seg_kernel(TopkArgs a) {
                           });
 }
 
-// Stage 2: one block per row selects among its nseg * k candidate slots.
-__global__ __launch_bounds__(512) void topk_cand_kernel(TopkArgs a) {
-  constexpr int NT = 512, EPT = kCandMax / NT;
+// Stage 2: one block per row selects among its nseg * k (<= 64 * NT) candidate slots.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a) {
+  constexpr int EPT = 64;
   __shared__ uint32_t hist[kHist];
   __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
   __shared__ uint32_t ctrl[4];
@@ -585,20 +591,27 @@ __global__ __launch_bounds__(512) void topk_cand_kernel(TopkArgs a) {
                       [&](uint32_t o, int c, uint32_t) { out[o] = ci[c]; });
 }
 
-// Segments per row for the two-stage path (0: the row fits one block or the
-// candidates of its segments would not fit stage 2).
-int topk_segments(int Lq, int q_start, int Lk, int k) {
+// Segment plan of the two-stage path: nseg segments of kSeg keys (wide =
+// false) or of kSegWide keys (wide = true); nseg = 0 when the row fits one
+// block or no plan holds the candidates.
+struct SegPlan {
+  int nseg;
+  bool wide;
+};
+SegPlan topk_plan(int Lq, int q_start, int Lk, int k) {
   const int max_n = min(q_start + Lq, Lk);
-  if (max_n <= kCandMax) return 0;
-  const int nseg = (max_n + kSeg - 1) / kSeg;
-  if ((long long)nseg * k > kCandMax || k % 4 != 0) return 0;
-  return nseg;
+  if (max_n <= kCandMax || k % 4 != 0) return {0, false};
+  const int narrow = (max_n + kSeg - 1) / kSeg;
+  if ((long long)narrow * k <= kCandMax) return {narrow, false};
+  const int wide = (max_n + kSegWide - 1) / kSegWide;
+  if ((long long)wide * k <= kCandWide) return {wide, true};
+  return {0, false};
 }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k) {
-  const int nseg = topk_segments(Lq, q_start, Lk, k);
+  const int nseg = topk_plan(Lq, q_start, Lk, k).nseg;
   return (size_t)B * Lq * nseg * k * (sizeof(uint32_t) + sizeof(int32_t));
 }
 
@@ -612,15 +625,23 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
       return launch_kernel((const void*)topk_reg_kernel<64, true, 512>, grid, dim3(512), 0, stream, a);
     return launch_kernel((const void*)topk_reg_kernel<64, false, 512>, grid, dim3(512), 0, stream, a);
   }
-  a.nseg = topk_segments(a.Lq, a.q_start, a.Lk, a.k);
+  const SegPlan plan = topk_plan(a.Lq, a.q_start, a.Lk, a.k);
+  a.nseg = plan.nseg;
   if (a.nseg > 0 && a.workspace) {
     a.cand_key = (uint32_t*)a.workspace;
     a.cand_idx = (int32_t*)(a.cand_key + (size_t)rows * a.nseg * a.k);
     const bool vec = a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0;
-    hipError_t e = launch_kernel(vec ? (const void*)topk_seg_kernel<true> : (const void*)topk_seg_kernel<false>,
-                                 dim3((unsigned)(rows * a.nseg)), dim3(kSegNT), 0, stream, a);
+    const dim3 sgrid((unsigned)(rows * a.nseg));
+    hipError_t e;
+    if (plan.wide)
+      e = launch_kernel(vec ? (const void*)topk_seg_kernel<64, 512, true> : (const void*)topk_seg_kernel<64, 512, false>,
+                        sgrid, dim3(512), 0, stream, a);
+    else
+      e = launch_kernel(vec ? (const void*)topk_seg_kernel<32, 256, true> : (const void*)topk_seg_kernel<32, 256, false>,
+                        sgrid, dim3(256), 0, stream, a);
     if (e != hipSuccess) return e;
-    return launch_kernel((const void*)topk_cand_kernel, grid, dim3(512), 0, stream, a);
+    if (plan.wide) return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a);
+    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a);
   }
   const size_t base = (size_t)(kBins + kWaves + 1 + 4) * sizeof(uint32_t);
   return launch_kernel((const void*)topk_kernel, grid, dim3(kThreads), base, stream, a);

@@ -260,7 +260,8 @@ def test_attention_dense_equivalence(dsa):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,n_random", [("prefill4k", 24), ("prefill32k", 16),
-                                            ("decode", 12), ("chunked", 12)])
+                                            ("decode", 12), ("chunked", 12),
+                                            ("decode1m", 2), ("chunked1m", 4)])
 def test_full_size_workloads(dsa, name, n_random):
     wl = dsa_inputs.WORKLOADS[name]
     log(f"[{name}] generating inputs")

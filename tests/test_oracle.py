@@ -394,3 +394,7 @@ def test_workload_pair_counts_closed_form():
     assert c["decode"].selected_pairs() == 64 * 2048
     assert c["chunked"].causal_pairs() == sum(range(122881, 131073))
     assert c["tiny"].selected_pairs() == 64 * 65 // 2 + (256 - 64) * 64
+    assert c["decode1m"].causal_pairs() == 4 * 2 ** 20
+    assert c["decode1m"].selected_pairs() == 4 * 2048
+    assert c["chunked1m"].causal_pairs() == sum(range(2 ** 20 - 4096 + 1, 2 ** 20 + 1))
+    assert c["chunked1m"].selected_pairs() == 4096 * 2048
