@@ -66,7 +66,8 @@ enum dsa_status {
 typedef struct dsa_problem {
   int32_t batch;       /* B  >= 1                                              */
   int32_t q_len;       /* Lq >= 1                                              */
-  int32_t kv_len;      /* Lk >= 1, q_start + q_len <= kv_len                    */
+  int32_t kv_len;      /* Lk >= 1, q_start + q_len <= kv_len; for the attention
+                          also Lk <= 2^24 and Lk * D_qk * 2 <= 4 GiB - 8 KiB  */
   int32_t q_start;     /* absolute position of query row 0 (>= 0)              */
   int32_t idx_heads;   /* H_I, 1..64                                           */
   int32_t idx_dim;     /* d_I: 32, 64, 96 or 128                                */
@@ -111,9 +112,13 @@ int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* 
  *   workspace: device scratch of at least dsa_workspace_size(p, DSA_OP_TOPK)
  *              bytes, 16-byte aligned (may be NULL when that size is 0).  It
  *              is non-zero when rows can exceed 32768 candidates: such rows are
- *              selected in two stages (top k of each 8192-key segment, then of
- *              their union), with B*Lq*ceil(max_row/8192)*k*8 bytes of
- *              candidates in between.  Contents on return are unspecified.
+ *              selected in two stages (top k of each segment, then of their
+ *              union), with B*Lq*nseg*k*8 bytes of candidates in between.
+ *              Segments hold 8192 keys while nseg*k <= 32768, else 32768 keys
+ *              while nseg*k <= 65536 (rows of up to 1,048,576 candidates at
+ *              k = 2048).  Longer rows need no workspace: they are selected by
+ *              passes that re-read the row.  Contents on return are
+ *              unspecified.
  */
 int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
              size_t workspace_bytes, void* stream);
@@ -153,8 +158,9 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
  * The scores live in the workspace (at least dsa_workspace_size(p,
  * DSA_OP_FORWARD) bytes, 256-byte aligned).  `indices` may be NULL; when given
  * ([B, Lq, k] int32) it receives the selection, otherwise the selection is
- * kept in the workspace.  Results are bit-identical to the three separate
- * calls.
+ * kept in the workspace, together with the top-k and attention scratch.
+ * Results are bit-identical to the three separate calls made with workspaces
+ * of the sizes dsa_workspace_size() reports for them.
  */
 int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
                 const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
