@@ -33,6 +33,8 @@
 #include "dsa_common.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace dsa {
 
 namespace {
@@ -214,11 +216,36 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
   const int QT = decode ? kDecodeQPW * kDecodeWaves / 4 : kPrefillQPW * kPrefillWaves;
   const int KS = decode ? 4 * kKeysPerWave : kKeysPerWave;
   a.n_qtiles = (a.Lq + QT - 1) / QT;
-  // Split long key ranges until there are enough blocks to fill the chip.
+  // Long key ranges are split over several blocks.  The splits write disjoint
+  // key ranges, but each one pays its own prologue (query operands, head
+  // weights, a first stage load that nothing hides), so a split is worth it
+  // only while the chip is under-filled or the grid's last round is.
+  //  - decode: one round of resident blocks (a 256-key stage pair takes
+  //    ~74 KB of LDS, so two blocks per CU): more rounds only add prologues.
+  //  - prefill: first at least two rounds (~5 blocks per CU) while a split
+  //    keeps >= 16 stages; then, because rows of equal length (chunked
+  //    prefill) end together and leave the last round part-empty, up to 32768
+  //    blocks while a split keeps >= 256 stages.  Causal rows from position 0
+  //    need no such help: their lengths differ and the longest start first.
+  // Measured on the 64 x 128 indexer: decode over 64 x 128K keys is fastest at
+  // 8 splits, over 4 x 1M at 128; prefill over 4K at 2, over 32K at 1, 8K new
+  // tokens of 128K at 4-8, 4K of 1M at 32.
   const long long tiles = (long long)a.B * a.n_qtiles;
   const int max_st = (a.Lk + KS - 1) / KS;
+  // Stages of an average tile: a tile's keys end at its last position.
+  const long long avg_st = ((long long)a.q_start + (a.Lq + 1) / 2 + KS - 1) / KS;
   int splits = 1;
-  while (tiles * splits < 2048 && splits * 2 <= max_st && splits < 64) splits *= 2;
+  auto grow = [&](long long blocks, long long min_stages) {
+    while (tiles * splits < blocks && splits * 2 <= max_st && avg_st >= 2LL * splits * min_stages)
+      splits *= 2;
+  };
+  if (decode) {
+    const long long per_cu = std::max<long long>(1, (160 * 1024) / (2LL * KS * (a.dI + 16)));
+    grow(256 * per_cu, 8);
+  } else {
+    grow(2 * 256 * 5, 16);
+    grow(32768, 256);
+  }
   a.n_splits = splits;
   const size_t smem = 2 * (size_t)KS * (a.dI + 16);
   const dim3 grid((unsigned)(tiles * splits));
