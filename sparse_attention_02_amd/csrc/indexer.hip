@@ -144,6 +144,11 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
 
   load_stage(st_begin);
   store_stage(0);
+  // The operand loads above sit in branches, so the compiler cannot prove
+  // they are complete when the loop starts; without this wait it drains every
+  // outstanding load, the next stage's prefetch included, before the first
+  // matrix product of each stage (13 % of the decode time).
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int st = st_begin; st < st_end; ++st) {
