@@ -43,7 +43,7 @@ namespace {
 constexpr int kChunk = 32;     // keys per chunk
 constexpr int kStages = 3;     // latent chunks in flight
 constexpr int kHeadTiles = 8;  // 128 heads / 16
-constexpr int kPRow = 64;      // bytes of one head's P row (32 bf16)
+constexpr int kPRow = 64;      // bytes of one head's P values (32 bf16)
 constexpr float kLazyMax = 8.0f;
 
 template <int DQK, int DV, int NW>
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   using S = AttnShape<DQK, DV, NW>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* kvb = smem;                                        // [kStages][CHUNK_BYTES]
-  uint8_t* pbuf = smem + kStages * S::CHUNK_BYTES;            // [2][128 heads][kPRow]
+  uint8_t* pbuf = smem + kStages * S::CHUNK_BYTES;            // [2][8 tiles][4 g][16 heads][16 B]
   float* alpha_s = (float*)(pbuf + 2 * S::P_BYTES);           // [2][16 lanes][8 head tiles]
   float* lsum_s = alpha_s + 2 * 128;                          // [128]
   int32_t* sidx = (int32_t*)(lsum_s + 128);                   // [nch * kChunk]
@@ -265,8 +265,11 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   const int r_v0 = 4 * g + (li >> 2);
   const int v_base = r_v0 * S::RS + 8 * (li & 1);
   const int v_sel = (li & 3) >> 1;
-  //  P row of head 16ht + li, piece g ^ ((head >> 2) & 3) == g ^ ((li >> 2) & 3)
-  const int p_off = li * kPRow + 16 * (g ^ ((li >> 2) & 3));
+  //  P is stored piece-major: the 16-byte piece g of head 16ht + li sits at
+  //  1024 ht + 256 g + 16 li, so both its writes and its reads are linear in
+  //  the lane index.  (A head-major layout with an XOR swizzle, balanced over
+  //  the 64 banks on paper, measured at half the LDS read rate.)
+  const int p_off = 256 * g + 16 * li;
 
   for (int it = 0; to_compute; ++it) {
     const int c = __builtin_ctzll(to_compute);
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       }
       l_part[ht] = l_part[ht] * al + psum;
       const int head = 16 * (S::HTQ * wave + ht) + li;
-      *(v4i*)(pbuf + pslot * S::P_BYTES + head * kPRow + 16 * (g ^ ((head >> 2) & 3))) =
+      *(v4i*)(pbuf + pslot * S::P_BYTES + 1024 * (head >> 4) + p_off) =
           (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
       if (g == 0) alpha_s[pslot * 128 + li * kHeadTiles + (head >> 4)] = al;
     }
