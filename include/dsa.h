@@ -114,11 +114,12 @@ int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* 
  *              is non-zero when rows can exceed 32768 candidates: such rows are
  *              selected in two stages (top k of each segment, then of their
  *              union), with B*Lq*nseg*k*8 bytes of candidates in between.
- *              Segments hold 8192 keys while nseg*k <= 32768, else 32768 keys
- *              while nseg*k <= 65536 (rows of up to 1,048,576 candidates at
- *              k = 2048).  Longer rows need no workspace: they are selected by
- *              passes that re-read the row.  Contents on return are
- *              unspecified.
+ *              Segments hold 32768 keys while nseg*k <= 65536 (rows of up to
+ *              1,048,576 candidates at k = 2048); 8192 keys instead when
+ *              nseg*k <= 32768 for them and B*Lq times the 32768-key segment
+ *              count is below 2048 (few rows, as in decode).  Longer rows need
+ *              no workspace: they are selected by passes that re-read the row.
+ *              Contents on return are unspecified.
  */
 int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
              size_t workspace_bytes, void* stream);

@@ -104,6 +104,13 @@ def test_workspace_sizes_and_forward_checks():
     dec = Problem(64, 1, 131072, 131071, 64, 128, 2048, 128, 512, 64)
     assert dsa.workspace_size(dec, dsa.DSA_OP_TOPK) == 64 * 16 * 2048 * 8
     assert dsa.workspace_size(dec, dsa.DSA_OP_SPARSE_MLA_ATTN) == 64 * 4 * 128 * 513 * 4
+    # many long rows (chunked prefill): 32K-key segments, 4 per 131K row
+    chunk = Problem(1, 8192, 131072, 122880, 64, 128, 2048, 128, 512, 64)
+    assert dsa.workspace_size(chunk, dsa.DSA_OP_TOPK) == 8192 * 4 * 2048 * 8
+    assert dsa.workspace_size(chunk, dsa.DSA_OP_SPARSE_MLA_ATTN) == 0
+    # 1M-key rows take 32 such segments whatever the row count
+    m1 = Problem(4, 1, 1048576, 1048575, 64, 128, 2048, 128, 512, 64)
+    assert dsa.workspace_size(m1, dsa.DSA_OP_TOPK) == 4 * 32 * 2048 * 8
     ws = dsa.workspace_size(MLA, dsa.DSA_OP_FORWARD)
     scores = 4096 * 4096 * 4
     idx = 4096 * 2048 * 4

@@ -145,17 +145,20 @@ def test_topk_sampled_threshold_paths(dsa, k):
     np.testing.assert_array_equal(idx.cpu().numpy()[0], ref)
 
 
-@pytest.mark.parametrize("k,Lk,Lq", [(64, 40000, 6), (2048, 40000, 4), (100, 65536, 3)])
+@pytest.mark.parametrize("k,Lk,Lq", [(64, 40000, 6), (2048, 40000, 4), (100, 65536, 3),
+                                     (64, 40000, 1024)])
 def test_topk_two_stage_long_rows(dsa, k, Lk, Lq):
     """Rows longer than one block holds go through per-segment selection and a
     merge; quantised scores put ties across segment boundaries, one row ends
-    exactly on a segment boundary and one just after it."""
-    rng = np.random.default_rng(k + Lk)
+    exactly on a segment boundary and one just after it.  A few rows use 8K-key
+    segments; 2048 rows (enough blocks) use 32K-key segments."""
+    rng = np.random.default_rng(k + Lk + Lq)
     B = 2
     q_start = Lk - Lq
     wl = dsa_inputs.Workload("long", 0, B, Lq, Lk, q_start, 4, 32, k, 8, 64, 16)
-    s = rng.integers(-40, 41, size=(B, Lq, Lk)).astype(np.float32) * 0.25
-    s[0, 0, 8192 - 5:8192 + 5] = 10.0   # a tie straddling the first segment boundary
+    s = rng.integers(-40, 41, size=(B, Lq, Lk), dtype=np.int8).astype(np.float32) * 0.25
+    s[0, 0, 8192 - 5:8192 + 5] = 10.0   # a tie straddling the first narrow segment boundary
+    s[0, 1, 32768 - 5:32768 + 5] = 10.0  # ... and the first wide one
     s[1, -1, :] = 3.0                    # an all-equal row: the k lowest indices win
     prob = dsa.Problem.from_workload(wl)
     ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
