@@ -64,6 +64,18 @@ struct AttnShape {
   static_assert(DQK % 8 == 0 && DTW >= 1 && DTW * 16 * NW == DV && DV <= DQK, "unsupported latent shape");
 };
 
+// q / d for 0 <= q < n as (q * ceil(2^19 / d)) >> 19: exact when every q in
+// range passes and q * multiplier fits 24 bits (both checked at compile time),
+// a full-rate 24-bit multiply where a division by a constant costs
+// quarter-rate multiply-highs.
+constexpr int kDivShift = 19;
+constexpr uint32_t div_mul(int d) { return ((1u << kDivShift) + (uint32_t)d - 1u) / (uint32_t)d; }
+constexpr bool div_mul_exact(int d, int n) {
+  for (int q = 0; q < n; ++q)
+    if ((int)(((uint32_t)q * div_mul(d)) >> kDivShift) != q / d) return false;
+  return (uint64_t)(n - 1) * div_mul(d) < (1u << 24);
+}
+
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -197,6 +209,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   const uint8_t* kv_bias = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK) - 4096;
   constexpr int NJ = (S::DMA_BLOCKS + NW - 1) / NW;
   static_assert(NJ <= 5 && S::DMA_BLOCKS / NW >= 1, "1 to 5 copies per wave and chunk");
+  static_assert(div_mul_exact(S::PPR, 64 * S::DMA_BLOCKS), "piece -> row split by multiply-shift");
   const int j_lo = wave * S::DMA_BLOCKS / NW;
   const bool long_run = (wave + 1) * S::DMA_BLOCKS / NW - j_lo == NJ;
   auto issue = [&](int c, int buf) {
@@ -212,7 +225,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     for (int j0 = 0; j0 < NJ; ++j0) {
       const int j = min(j_lo + j0, S::DMA_BLOCKS - 1);
       const int p = 64 * j + ln;
-      const int r = p / S::PPR, pp = p % S::PPR;
+      const int r = (int)(__umul24((uint32_t)p, div_mul(S::PPR)) >> kDivShift);
+      const int pp = p - (int)__umul24((uint32_t)r, S::PPR);
       const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
       const int src_col = lp < S::RPR ? lp : lp - S::RPR;  // pad pieces meet zero q
       const int idx = max(sidx[c * kChunk + r], 0);
@@ -317,23 +331,30 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     }
 
     // ---- softmax for this lane's heads over its 8 keys; P and alpha -> LDS
+    // Raw scores; the scale (> 0, so it keeps the order) is applied to the
+    // maximum and folded into the exponent's FMA.  Only chunks holding
+    // invalid entries (-1 padding) are masked: a wave-uniform branch.
     const bool full = (full_mask >> c) & 1;
-    v4i id0 = {0, 0, 0, 0}, id1 = {0, 0, 0, 0};
-    if (!full) {
-      id0 = *(const v4i*)(sidx + c * kChunk + 4 * g);
-      id1 = *(const v4i*)(sidx + c * kChunk + 16 + 4 * g);
-    }
 #pragma unroll
     for (int ht = 0; ht < S::HTQ; ++ht) {
       float z[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        z[r] = id0[r] >= 0 ? s[ht][0][r] * a.scale_log2 : -INFINITY;
-        z[4 + r] = id1[r] >= 0 ? s[ht][1][r] * a.scale_log2 : -INFINITY;
+        z[r] = s[ht][0][r];
+        z[4 + r] = s[ht][1][r];
+      }
+      if (!full) {
+        const v4i id0 = *(const v4i*)(sidx + c * kChunk + 4 * g);
+        const v4i id1 = *(const v4i*)(sidx + c * kChunk + 16 + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          z[r] = id0[r] >= 0 ? z[r] : -INFINITY;
+          z[4 + r] = id1[r] >= 0 ? z[4 + r] : -INFINITY;
+        }
       }
       float mloc = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
                          fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
-      mloc = max_xor32(max_xor16(mloc));
+      mloc = max_xor32(max_xor16(mloc)) * a.scale_log2;
       float al = 1.0f;
       if (mloc > m_use[ht] + kLazyMax) {
         al = fast_exp2(m_use[ht] - mloc);
@@ -343,8 +364,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       float psum = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(z[2 * i] - m_use[ht]);
-        const float p1 = fast_exp2(z[2 * i + 1] - m_use[ht]);
+        const float p0 = fast_exp2(fmaf(z[2 * i], a.scale_log2, -m_use[ht]));
+        const float p1 = fast_exp2(fmaf(z[2 * i + 1], a.scale_log2, -m_use[ht]));
         psum += p0 + p1;
         pk[i] = pack_bf16x2(p0, p1);
       }
