@@ -224,11 +224,15 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int j0 = 0; j0 < NJ; ++j0) {
       const int j = min(j_lo + j0, S::DMA_BLOCKS - 1);
-      const int p = 64 * j + ln;
-      const int r = (int)(__umul24((uint32_t)p, div_mul(S::PPR)) >> kDivShift);
-      const int pp = p - (int)__umul24((uint32_t)r, S::PPR);
-      const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
-      const int src_col = lp < S::RPR ? lp : lp - S::RPR;  // pad pieces meet zero q
+      const uint32_t p = 64u * (uint32_t)j + (uint32_t)ln;
+      const uint32_t r = __umul24(p, div_mul(S::PPR)) >> kDivShift;
+      const uint32_t pp = p - r * (uint32_t)S::PPR;
+      const uint32_t lp = S::SWZ ? (pp ^ (r & 7u)) : pp;
+      // Pad pieces (score width rounded up to 32) re-read real ones; they
+      // meet zero q.  The swizzle keeps a piece inside its aligned group of
+      // 8, so without padding every piece is a real one.
+      uint32_t src_col = lp;
+      if constexpr (S::PPR != S::RPR) src_col = lp < (uint32_t)S::RPR ? lp : lp - S::RPR;
       const int idx = max(sidx[c * kChunk + r], 0);
       // row indices are < 2^24 and the cache is < 4 GiB - 8 KiB (checked by the host)
       off[j0] = __umul24((uint32_t)idx, DQK * 2) + 16 * src_col + 4096 - 1024 * (j0 - 2);
