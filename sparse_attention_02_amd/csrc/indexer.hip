@@ -8,7 +8,15 @@
 // Mapping.  The contraction runs as a GEMM whose rows are (query, head) pairs
 // and whose columns are keys: one v_mfma_f32_16x16x128_f8f6f4 multiplies 16
 // heads of one query by 16 keys over the whole d_I = 128 (shorter d_I is zero
-// padded).  Each lane then owns 4 heads x 1 key of the 16x16 result, applies
+// padded).  The product sums over d, so the d-bytes may be dealt to the lanes
+// in any order both operands share.  Decode deals lane group g the bytes
+// [32g, 32g+32) and keeps 144-byte padded key rows in LDS; prefill deals it
+// [16g, 16g+16) and [64+16g, 64+16g+16) over 128-byte rows whose 16-byte
+// pieces are XOR-swizzled by (row & 7), which spreads a wave's key reads
+// evenly over the 64 LDS banks (the contiguous order runs them 2-way
+// conflicted).  Decode keeps the contiguous order: the swizzled one needs a
+// second read address per key tile, and the decode variant has no register
+// left for it.  Each lane then owns 4 heads x 1 key of the 16x16 result, applies
 // the ReLU and the head weight in registers and keeps a running partial sum;
 // partial sums over the four lane groups are combined with two butterfly
 // exchanges that also spread the 4 key tiles so that lane l ends with key l of
@@ -47,7 +55,7 @@ constexpr int kKeysPerWave = 64;
 // queries and weights).  A compile-time count keeps the MFMA sequence free of
 // branches, so the 2 * NHG products of a key tile are issued back to back into
 // separate accumulators before their epilogues read them.
-// FULLD: d_I == 128, every lane group holds 32 bytes of the key row.
+// FULLD: d_I == 128, every lane group's 32 bytes are present.
 // ReLU as a single v_max_f32.  This file is compiled without NaN semantics
 // (the scores of NaN inputs are undefined): with them, fmaxf(x, 0) costs two
 // VALU operations (a NaN-quieting canonicalisation of x, then the max), and
@@ -85,9 +93,14 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
   if (st_begin >= st_end) return;
 
   const int dI = a.dI;
-  const int row_bytes = dI + 16;        // padded LDS row
+  constexpr bool SWZ = NKL == 1;        // prefill: swizzled 128-byte rows (see above)
+  const int row_bytes = SWZ ? 128 : dI + 16;
   const int stage_bytes = KS * row_bytes;
-  const bool g_active = 32 * g < dI;
+  // d-bytes of this lane group: [off_lo, off_lo + 16) and [off_hi, off_hi + 16)
+  const int off_lo = SWZ ? 16 * g : 32 * g;
+  const int off_hi = SWZ ? 64 + 16 * g : 32 * g + 16;
+  const bool lo_ok = FULLD || off_lo < dI;
+  const bool hi_ok = FULLD || off_hi < dI;
 
   // ---- A operands (query heads) and head weights, resident for the whole block
   v8i qa[kQPW][NHG];
@@ -99,10 +112,11 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
     for (int hg = 0; hg < NHG; ++hg) {
       const int head = 16 * hg + (lane & 15);
       v8i v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (t < a.Lq && head < a.HI && g_active) {
-        const uint8_t* src = a.q_idx + (((size_t)b * a.Lq + t) * a.HI + head) * dI + 32 * g;
-        const v4i* s4 = (const v4i*)src;
-        v4i lo = s4[0], hi = s4[1];
+      if (t < a.Lq && head < a.HI) {
+        const uint8_t* src = a.q_idx + (((size_t)b * a.Lq + t) * a.HI + head) * dI;
+        const v4i zero = {0, 0, 0, 0};
+        const v4i lo = lo_ok ? *(const v4i*)(src + off_lo) : zero;
+        const v4i hi = hi_ok ? *(const v4i*)(src + off_hi) : zero;
         v = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       qa[q][hg] = v;
@@ -137,8 +151,10 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
 #pragma unroll
     for (int j = 0; j < kMaxPieces; ++j) {
       const int p = threadIdx.x + j * kThreads;
-      if (p < stage_pieces)
-        *(v4i*)(dst + (p / pieces_per_row) * row_bytes + 16 * (p % pieces_per_row)) = pf[j];
+      if (p < stage_pieces) {
+        const int r = p / pieces_per_row, q = p % pieces_per_row;
+        *(v4i*)(dst + r * row_bytes + 16 * (SWZ ? q ^ (r & 7) : q)) = pf[j];
+      }
     }
   };
 
@@ -165,12 +181,23 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       const int key_local = kKeysPerWave * klane + 16 * kt + (lane & 15);
-      // With d_I < 128 the lane groups past d_I read the row's first bytes and
-      // use zeros (stale bytes could be FP8 NaNs, and 0 * NaN is NaN).
-      const bool ld = FULLD || g_active;
-      const v4i* s4 = (const v4i*)(sb + key_local * row_bytes + (ld ? 32 * g : 0));
-      v4i lo = s4[0], hi4 = s4[1];
-      if (!FULLD && !g_active) lo = hi4 = (v4i){0, 0, 0, 0};
+      // With d_I < 128, pieces past d_I are read from within the row (stale
+      // bytes, or the row's first bytes) and replaced by zeros (stale bytes
+      // could be FP8 NaNs, and 0 * NaN is NaN).  Swizzled rows: pieces g and
+      // g + 4 of row key_local, whose & 7 is lane & 7.
+      const uint8_t* row = sb + key_local * row_bytes;
+      v4i lo, hi4;
+      if constexpr (SWZ) {
+        const int o = 16 * (g ^ (lane & 7));
+        lo = *(const v4i*)(row + o);
+        hi4 = *(const v4i*)(row + (o ^ 64));
+      } else {
+        const v4i* s4 = (const v4i*)(row + (lo_ok ? off_lo : 0));
+        lo = s4[0];
+        hi4 = s4[1];
+      }
+      if (!lo_ok) lo = (v4i){0, 0, 0, 0};
+      if (!hi_ok) hi4 = (v4i){0, 0, 0, 0};
       const v8i kb = (v8i){lo[0], lo[1], lo[2], lo[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       v4f x[kQPW][NHG];
 #pragma unroll
@@ -252,7 +279,7 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
     grow(32768, 256);
   }
   a.n_splits = splits;
-  const size_t smem = 2 * (size_t)KS * (a.dI + 16);
+  const size_t smem = 2 * (size_t)KS * (decode ? a.dI + 16 : 128);  // two stages of key rows
   const dim3 grid((unsigned)(tiles * splits));
   const int nhg = (a.HI + 15) >> 4;
   const bool full = a.dI == 128;
