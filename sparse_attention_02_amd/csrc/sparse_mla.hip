@@ -145,7 +145,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   // ones instead of one at a time, and their gathers meet in the same L2;
   // runs rather than one range per XCD keep the causal rows' uneven work
   // spread over all XCDs.  Blocks past the last whole round keep their index.
-  constexpr int kXcdRun = 16;
+  constexpr int kXcdRun = 32;  // swept 8..128 at L=32K and L=4K: 32 best
   const int nb = gridDim.x;
   const int full = nb / (8 * kXcdRun) * (8 * kXcdRun);
   const int xi = blockIdx.x >> 3;
