@@ -9,6 +9,10 @@ synthetic and resident in HBM before timing starts.
 
 Prints one JSON line: query tokens/s, per-kernel times and rooflines, and the
 CPU oracle timed on a bounded row sample of the same workload.
+
+--attn masked replaces the sparse attention by dsa_masked_mha_attn (the masked
+mode for short prefill: dense over each query's causal range, non-selected
+tokens masked); its roofline counts that dense work.
 """
 from __future__ import annotations
 
@@ -31,6 +35,7 @@ KERNEL_SOURCES = {
     "index_scores": "sparse_attention_02_amd/csrc/indexer.hip",
     "topk": "sparse_attention_02_amd/csrc/topk.hip",
     "sparse_mla_attn": "sparse_attention_02_amd/csrc/sparse_mla.hip",
+    "masked_mha_attn": "sparse_attention_02_amd/csrc/sparse_mla.hip",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 COPY_BYTES = 1 << 30  # calibration copy: reads and writes exactly this many bytes
@@ -42,6 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k")
+    ap.add_argument("--attn", choices=["sparse", "masked"], default="sparse",
+                    help="attention stage: the sparse kernel, or the masked mode for short prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
@@ -72,6 +79,13 @@ def algorithmic(wl):
             flop=2.0 * wl.heads * (wl.d_qk + wl.d_latent) * sel,
             bytes=rows * wl.heads * (2 * wl.d_qk + 4 * wl.d_latent + 4) + 4.0 * rows * wl.topk
             + 2.0 * wl.d_qk * sel),
+        # the masked mode scores every causal pair and runs the value product on
+        # all of them (masked probabilities are zero); it reads each latent row
+        # of the causal range once per query
+        "masked_mha_attn": dict(
+            flop=2.0 * wl.heads * (wl.d_qk + wl.d_latent) * causal,
+            bytes=rows * wl.heads * (2 * wl.d_qk + 4 * wl.d_latent + 4) + 4.0 * rows * wl.topk
+            + 2.0 * wl.d_qk * causal),
     }
 
 
@@ -161,7 +175,8 @@ def main():
     aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    names = ["index_scores", "topk", "sparse_mla_attn"]
+    attn_name = "sparse_mla_attn" if args.attn == "sparse" else "masked_mha_attn"
+    names = ["index_scores", "topk", attn_name]
 
     def step(ev=None):
         if ev is not None:
@@ -172,7 +187,10 @@ def main():
         dsa.dsa_topk(prob, scores, indices, ws, ws_bytes, stream=stream)
         if ev is not None:
             ev[2].record(stream)
-        dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
+        if args.attn == "sparse":
+            dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
+        else:
+            dsa.dsa_masked_mha_attn(prob, q, kv, indices, out, lse, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 
@@ -251,7 +269,7 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len, "kv_len": wl.kv_len,
                    "q_start": wl.q_start, "topk": wl.topk, "idx_heads": wl.idx_heads,
                    "idx_dim": wl.idx_dim, "heads": wl.heads, "d_latent": wl.d_latent,
-                   "d_rope": wl.d_rope},
+                   "d_rope": wl.d_rope, "attn": args.attn},
         "roofline": roof,
         "indexer_fp8_tflops": kernels["index_scores"]["tflops"],
         "indexer_frac_of_fp8_peak": kernels["index_scores"]["frac_of_mfma_peak"],

@@ -86,6 +86,9 @@ WORKLOADS: Dict[str, Workload] = {
     # 1M-token contexts (the indexer's surviving quadratic term at long context)
     "decode1m": Workload("decode1m", 5, 4, 1, 1048576, 1048575, 64, 128, 2048, 128, 512, 64),
     "chunked1m": Workload("chunked1m", 6, 1, 4096, 1048576, 1044480, 64, 128, 2048, 128, 512, 64),
+    # short prefill, every row selects its whole causal prefix (L <= k): the
+    # regime of the masked mode
+    "prefill2k": Workload("prefill2k", 7, 1, 2048, 2048, 0, 64, 128, 2048, 128, 512, 64),
 }
 
 

@@ -18,6 +18,9 @@
  *                        head, one selection per query position (lightning
  *                        indexer post, same section; spec sheet, "Inference
  *                        efficiency" table, KV-cache design).
+ *   dsa_masked_mha_attn  the same attention computed densely over each
+ *                        query's causal range with the non-selected tokens
+ *                        masked: the masked mode for short prefill.
  *   dsa_forward          the three stages in order on one stream.
  *
  * Conventions shared by every entry point
@@ -153,6 +156,26 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
 int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
                         const int32_t* indices, float* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Masked mode for short prefill: the same attention as dsa_sparse_mla_attn,
+ * computed densely.  The pages name a masked MHA mode that simulates DSA for
+ * short-sequence prefill without specifying it (DeepSeek-V3.2 spec sheet,
+ * design overview; "Inference efficiency" table, serving optimisations); the
+ * reading taken here: for every (b, t, h), the scores of ALL tokens
+ * s = 0 .. pos(t) are computed from contiguous latent rows and those not in
+ * the selection are masked out of the softmax, so
+ *   out[b,t,h,:], lse[b,t,h] = attention over { s <= pos(t) : s in indices[b,t,:] }
+ * Entries that are -1, out of range or past pos(t) are ignored and a repeated
+ * entry counts once; for selections made by dsa_topk (distinct, <= pos(t))
+ * this equals dsa_sparse_mla_attn within rounding.  A row with no selected
+ * entry gives out = 0, lse = -inf.  Work grows with pos(t) rather than k.
+ *
+ *   q, kv, indices, out, lse: as for dsa_sparse_mla_attn.
+ * Requires kv_len <= 65536 (DSA_ERR_UNSUPPORTED otherwise).  No workspace.
+ */
+int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                        const int32_t* indices, float* out, float* lse, void* stream);
 
 /*
  * dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.

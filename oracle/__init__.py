@@ -56,6 +56,9 @@ def lib():
         L.dsa_oracle_sparse_mla_attn.argtypes = [i32, i32, i32, i32, i32, f32, i64,
                                                  vp, vp, vp, vp, vp, vp]
         L.dsa_oracle_sparse_mla_attn.restype = None
+        L.dsa_oracle_masked_mha_attn.argtypes = [i32, i32, i32, i32, i32, f32, i64,
+                                                 vp, vp, vp, vp, vp, vp, vp]
+        L.dsa_oracle_masked_mha_attn.restype = None
         L.dsa_oracle_max_threads.argtypes = []
         L.dsa_oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -146,6 +149,32 @@ def sparse_mla_attn(kv, q_rows, indices, row_batch, d_latent: int, softmax_scale
     lse = np.empty((R, H), dtype=np.float32)
     lib().dsa_oracle_sparse_mla_attn(Lk, H, d_latent, Dqk - d_latent, k, float(softmax_scale), R,
                                      rbp, qp, kv.ctypes.data, ip, out.ctypes.data, lse.ctypes.data)
+    return out, lse
+
+
+def masked_mha_attn(kv, q_rows, indices, row_batch, row_pos, d_latent: int, softmax_scale: float):
+    """Masked mode for short prefill, in double precision: dense causal attention
+    over s = 0 .. pos with the tokens outside the row's indices masked to -inf
+    (DeepSeek-V3.2 spec sheet, design overview and "Inference efficiency":
+    a masked MHA mode simulating DSA for short-sequence prefill).  Arguments as
+    for sparse_mla_attn plus row_pos [R]; entries outside [0, min(pos+1, Lk))
+    are ignored and a listed token counts once.  Returns (out, lse)."""
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    B, Lk, Dqk = kv.shape
+    q_rows, qp = _c(q_rows, np.uint16)
+    R, H, Dqk2 = q_rows.shape
+    assert Dqk2 == Dqk and 0 < d_latent <= Dqk
+    indices, ip = _c(indices, np.int32)
+    assert indices.shape[0] == R
+    k = indices.shape[1]
+    rb, rbp = _c(row_batch, np.int32)
+    rpos, rpp = _c(row_pos, np.int32)
+    assert (rb >= 0).all() and (rb < B).all() and rpos.shape == (R,) and (rpos >= 0).all()
+    out = np.empty((R, H, d_latent), dtype=np.float32)
+    lse = np.empty((R, H), dtype=np.float32)
+    lib().dsa_oracle_masked_mha_attn(Lk, H, d_latent, Dqk - d_latent, k, float(softmax_scale), R,
+                                     rbp, rpp, qp, kv.ctypes.data, ip, out.ctypes.data,
+                                     lse.ctypes.data)
     return out, lse
 
 

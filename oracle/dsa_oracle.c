@@ -28,6 +28,14 @@
  *    selected latents only, in double precision; the value is the first
  *    d_latent columns of each latent row and the scores use all
  *    d_latent + d_rope columns.
+ *  - Masked mode for short prefill (DeepSeek-V3.2 spec sheet, design overview
+ *    and "Inference efficiency" table: a masked MHA mode simulates DSA for
+ *    short-sequence prefill; the pages do not specify it).  Reading: the same
+ *    heads attend densely to every token s <= pos(t) and the scores of the
+ *    tokens outside the selection are set to -inf before the softmax.  It is
+ *    written here as that dense masked softmax, separately from the sparse
+ *    function above, so that the two formulations can be checked against
+ *    each other.
  *
  * Query rows are given explicitly (batch index, absolute position and the
  * row's own query data), so any subset of a workload's rows can be evaluated.
@@ -187,6 +195,57 @@ void dsa_oracle_sparse_mla_attn(int32_t kv_len, int32_t heads, int32_t d_latent,
       float* o = out + (r * heads + h) * d_latent;
       for (int d = 0; d < d_latent; ++d) o[d] = Z > 0.0 ? (float)(acc[d] / Z) : 0.0f;
       if (lse) lse[r * heads + h] = Z > 0.0 ? (float)(zmax + log(Z)) : -INFINITY;
+      free(qh);
+      free(z);
+      free(acc);
+    }
+  }
+}
+
+/* Dense causal attention of each (row, head) over s = 0 .. min(pos, kv_len - 1)
+ * with the scores of the tokens not listed in the row's indices set to -inf
+ * (entries outside that range are ignored; a listed token counts once). */
+void dsa_oracle_masked_mha_attn(int32_t kv_len, int32_t heads, int32_t d_latent, int32_t d_rope,
+                                int32_t topk, float softmax_scale, int64_t nrows,
+                                const int32_t* row_batch, const int32_t* row_pos,
+                                const uint16_t* q_rows, const uint16_t* kv, const int32_t* indices,
+                                float* out, float* lse) {
+  const int32_t dqk = d_latent + d_rope;
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int64_t r = 0; r < nrows; ++r) {
+    for (int32_t h = 0; h < heads; ++h) {
+      const uint16_t* cache = kv + (int64_t)row_batch[r] * kv_len * dqk;
+      const int32_t n = row_pos[r] + 1 < kv_len ? row_pos[r] + 1 : kv_len;
+      unsigned char* keep = (unsigned char*)calloc((size_t)n, 1);
+      double* z = (double*)malloc((size_t)n * sizeof(double));
+      double* acc = (double*)calloc((size_t)d_latent, sizeof(double));
+      double* qh = (double*)malloc((size_t)dqk * sizeof(double));
+      for (int i = 0; i < topk; ++i) {
+        const int32_t s = indices[r * topk + i];
+        if (s >= 0 && s < n) keep[s] = 1;
+      }
+      for (int d = 0; d < dqk; ++d) qh[d] = bf16_to_double(q_rows[(r * heads + h) * dqk + d]);
+      /* the dense scores, then the mask */
+      double zmax = -INFINITY;
+      for (int32_t s = 0; s < n; ++s) {
+        const uint16_t* row = cache + (int64_t)s * dqk;
+        double dot = 0.0;
+        for (int d = 0; d < dqk; ++d) dot += qh[d] * bf16_to_double(row[d]);
+        z[s] = keep[s] ? (double)softmax_scale * dot : -INFINITY;
+        if (z[s] > zmax) zmax = z[s];
+      }
+      double Z = 0.0;
+      if (zmax > -INFINITY)
+        for (int32_t s = 0; s < n; ++s) {
+          const double p = exp(z[s] - zmax);
+          Z += p;
+          const uint16_t* row = cache + (int64_t)s * dqk;
+          for (int d = 0; d < d_latent; ++d) acc[d] += p * bf16_to_double(row[d]);
+        }
+      float* o = out + (r * heads + h) * d_latent;
+      for (int d = 0; d < d_latent; ++d) o[d] = Z > 0.0 ? (float)(acc[d] / Z) : 0.0f;
+      if (lse) lse[r * heads + h] = Z > 0.0 ? (float)(zmax + log(Z)) : -INFINITY;
+      free(keep);
       free(qh);
       free(z);
       free(acc);

@@ -77,8 +77,10 @@ def _load():
     L.dsa_index_scores.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_forward):
+    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_masked_mha_attn,
+              L.dsa_forward):
         f.restype = i32
     L.dsa_workspace_size.argtypes = [P, i32]
     L.dsa_workspace_size.restype = sz
@@ -145,6 +147,13 @@ def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, workspa
     _check(lib.dsa_sparse_mla_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
                                    _stream(stream)))
+
+
+def dsa_masked_mha_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:
+    """The same attention computed densely over each query's causal range with the
+    non-selected tokens masked (include/dsa.h: dsa_masked_mha_attn)."""
+    _check(lib.dsa_masked_mha_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
+                                   _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def dsa_forward(problem: Problem, q_idx, k_idx, w, q, kv, out, lse=None, indices=None,

@@ -24,6 +24,7 @@ int fail(int status, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaskedMaxKv = 65536;  // masked attention: longest causal range (LDS bitmap)
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -122,7 +123,7 @@ dsa::AttnArgs attn_args(const dsa_problem* p, const uint16_t* q, const uint16_t*
   dsa::AttnArgs a{};
   a.q = q; a.kv = kv; a.indices = indices; a.out = out; a.lse = lse;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.H = p->heads;
-  a.Dv = p->d_latent; a.Dr = p->d_rope; a.k = p->topk;
+  a.Dv = p->d_latent; a.Dr = p->d_rope; a.k = p->topk; a.q_start = p->q_start;
   a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
   a.nsplit = 1;
   const size_t need = attn_ws_bytes(p);
@@ -220,6 +221,23 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
                         attn_args(p, q, kv, indices, out, lse, workspace, workspace_bytes),
                         (hipStream_t)stream),
                     "sparse_mla_attn launch");
+}
+
+int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                        const int32_t* indices, float* out, float* lse, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_attn(p)) return s;
+  // the selection bitmap of a row (one bit per key) sits in LDS
+  if (p->kv_len > kMaskedMaxKv)
+    return fail(DSA_ERR_UNSUPPORTED, "masked mode: kv_len %d > %d", p->kv_len, kMaskedMaxKv);
+  if (int s = check_ptr(q, "q", 16)) return s;
+  if (int s = check_ptr(kv, "kv", 16)) return s;
+  if (int s = check_ptr(indices, "indices", 16)) return s;
+  if (int s = check_ptr(out, "out", 16)) return s;
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_ALIGN, "lse is not 4-byte aligned");
+  return hip_status(dsa::launch_masked_mha_attn(attn_args(p, q, kv, indices, out, lse, nullptr, 0),
+                                                (hipStream_t)stream),
+                    "masked_mha_attn launch");
 }
 
 int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,

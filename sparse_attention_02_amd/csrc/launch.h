@@ -35,6 +35,7 @@ struct AttnArgs {
   float* out;               // [B, Lq, H, Dv]
   float* lse;               // [B, Lq, H] or null
   int B, Lq, Lk, H, Dv, Dr, k;
+  int q_start;              // position of query row 0 (masked mode)
   float scale_log2;         // softmax_scale * log2(e)
   // split over the selected chunks (nsplit > 1): block (row, part) writes the
   // attention over its share of the chunks, normalised, with its lse, to
@@ -57,6 +58,9 @@ hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k);
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream);
+// Masked mode for short prefill: dense over the causal range, masked to the
+// selection (no split: nsplit must be 1).
+hipError_t launch_masked_mha_attn(const AttnArgs& a, hipStream_t stream);
 // Parts per row when few rows would leave most CUs idle (1: no split), and the
 // workspace the split needs.
 int attn_splits(int rows, int k);

@@ -124,7 +124,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-template <int DQK, int DV, int NW>
+// MASKED: the masked mode for short prefill.  The row's whole causal range
+// [0, pos(t)] is streamed in contiguous chunks and the entries outside the
+// selection are masked in the softmax, instead of gathering the selected rows.
+template <int DQK, int DV, int NW, bool MASKED>
 __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   using S = AttnShape<DQK, DV, NW>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -133,6 +136,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   float* alpha_s = (float*)(pbuf + 2 * S::P_BYTES);           // [2][16 lanes][8 head tiles]
   float* lsum_s = alpha_s + 2 * 128;                          // [128]
   int32_t* sidx = (int32_t*)(lsum_s + 128);                   // [nch * kChunk]
+  uint32_t* selm = (uint32_t*)sidx;  // masked mode: [nch] selection bit per key of a chunk
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -155,7 +159,9 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   const int row = vb / a.nsplit;
   const int part = vb % a.nsplit;
   const int b = row / a.Lq;
-  const int nch = (a.k + kChunk - 1) / kChunk;
+  // masked mode: the row's causal range [0, n_keys) in chunks of kChunk keys
+  const int n_keys = MASKED ? min(a.q_start + row % a.Lq + 1, a.Lk) : 0;
+  const int nch = ((MASKED ? n_keys : a.k) + kChunk - 1) / kChunk;
   // chunks [c_lo, c_hi) of the row belong to this block
   const int c_lo = part * nch / a.nsplit, c_hi = (part + 1) * nch / a.nsplit;
   float* out_base = a.nsplit > 1 ? a.part_out + (size_t)vb * a.H * DV
@@ -163,15 +169,26 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)vb * a.H
                                  : (a.lse ? a.lse + (size_t)row * a.H : nullptr);
 
-  // ---- selected indices -> LDS (entries outside [0, Lk) become -1)
+  uint64_t chunk_mask = 0, full_mask = 0;  // sparse: chunks with some / with only valid entries
   const int32_t* idx_row = a.indices + (size_t)row * a.k;
-  for (int i = c_lo * kChunk + threadIdx.x; i < c_hi * kChunk; i += blockDim.x) {
-    const int v = i < a.k ? idx_row[i] : -1;
-    sidx[i] = (v >= 0 && v < a.Lk) ? v : -1;
-  }
-  __syncthreads();
-  uint64_t chunk_mask, full_mask;  // chunks with some / with only valid entries
-  {
+  if constexpr (MASKED) {
+    // ---- selection bitmap of this block's chunks (entries outside its key
+    // range, past pos(t) included, are not set; a repeated entry counts once)
+    for (int i = c_lo + threadIdx.x; i < c_hi; i += blockDim.x) selm[i] = 0u;
+    __syncthreads();
+    const int s_lo = kChunk * c_lo, s_hi = min(kChunk * c_hi, n_keys);
+    for (int i = threadIdx.x; i < a.k; i += blockDim.x) {
+      const int v = idx_row[i];
+      if (v >= s_lo && v < s_hi) atomicOr(&selm[v / kChunk], 1u << (v % kChunk));
+    }
+    __syncthreads();
+  } else {
+    // ---- selected indices -> LDS (entries outside [0, Lk) become -1)
+    for (int i = c_lo * kChunk + threadIdx.x; i < c_hi * kChunk; i += blockDim.x) {
+      const int v = i < a.k ? idx_row[i] : -1;
+      sidx[i] = (v >= 0 && v < a.Lk) ? v : -1;
+    }
+    __syncthreads();
     const bool mine = lane >= c_lo && lane < c_hi;
     bool any = false, all = mine;
     if (mine)
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       // 8, so without padding every piece is a real one.
       uint32_t src_col = lp;
       if constexpr (S::PPR != S::RPR) src_col = lp < (uint32_t)S::RPR ? lp : lp - S::RPR;
-      const int idx = max(sidx[c * kChunk + r], 0);
+      const int idx = MASKED ? min(kChunk * c + (int)r, n_keys - 1) : max(sidx[c * kChunk + r], 0);
       // row indices are < 2^24 and the cache is < 4 GiB - 8 KiB (checked by the host)
       off[j0] = __umul24((uint32_t)idx, DQK * 2) + 16 * src_col + 4096 - 1024 * (j0 - 2);
     }
@@ -258,16 +275,21 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     l_part[ht] = 0.0f;
   }
 
-  uint64_t to_issue = chunk_mask;
-  uint64_t to_compute = chunk_mask;
-  const int total = __builtin_popcountll(chunk_mask);
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) {
-    if (to_issue) {
-      issue(__builtin_ctzll(to_issue), s);
+  // The chunks this block computes, in order: the set bits of chunk_mask, or
+  // in masked mode every chunk c_lo .. c_hi - 1.
+  uint64_t to_issue = chunk_mask, to_compute = chunk_mask;
+  int next_issue = c_lo;
+  const int total = MASKED ? c_hi - c_lo : __builtin_popcountll(chunk_mask);
+  auto issue_next = [&](int slot) {
+    if constexpr (MASKED) {
+      if (next_issue < c_hi) issue(next_issue++, slot);
+    } else if (to_issue) {
+      issue(__builtin_ctzll(to_issue), slot);
       to_issue &= to_issue - 1;
     }
-  }
+  };
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue_next(s);
 
   // Per-lane LDS byte offsets of the operand reads.  With the swizzle, logical
   // piece lp of row r sits at piece lp ^ (r & 7): 8*(lp>>3) + ((lp&7) ^ (r&7)).
@@ -289,9 +311,14 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   //  the 64 banks on paper, measured at half the LDS read rate.)
   const int p_off = 256 * g + 16 * li;
 
-  for (int it = 0; to_compute; ++it) {
-    const int c = __builtin_ctzll(to_compute);
-    to_compute &= to_compute - 1;
+  for (int it = 0; it < total; ++it) {
+    int c;
+    if constexpr (MASKED) {
+      c = c_lo + it;
+    } else {
+      c = __builtin_ctzll(to_compute);
+      to_compute &= to_compute - 1;
+    }
     const int buf = it % kStages;
     const uint8_t* kb = kvb + buf * S::CHUNK_BYTES;
     const int pslot = it & 1;
@@ -337,8 +364,13 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     // ---- softmax for this lane's heads over its 8 keys; P and alpha -> LDS
     // Raw scores; the scale (> 0, so it keeps the order) is applied to the
     // maximum and folded into the exponent's FMA.  Only chunks holding
-    // invalid entries (-1 padding) are masked: a wave-uniform branch.
-    const bool full = (full_mask >> c) & 1;
+    // invalid entries (-1 padding) are masked: a wave-uniform branch.  In
+    // masked mode chunks not wholly selected are masked by their bits; a head's
+    // maximum stays -inf until a selected entry is seen, and while it does
+    // every score is -inf and is taken against 0 (giving p = 0, not NaN).
+    uint32_t bits = 0;
+    if constexpr (MASKED) bits = __builtin_amdgcn_readfirstlane(selm[c]);
+    const bool full = MASKED ? bits == 0xFFFFFFFFu : (full_mask >> c) & 1;
 #pragma unroll
     for (int ht = 0; ht < S::HTQ; ++ht) {
       float z[8];
@@ -347,7 +379,13 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
         z[r] = s[ht][0][r];
         z[4 + r] = s[ht][1][r];
       }
-      if (!full) {
+      if (MASKED && !full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          z[r] = (bits >> (4 * g + r)) & 1u ? z[r] : -INFINITY;
+          z[4 + r] = (bits >> (16 + 4 * g + r)) & 1u ? z[4 + r] : -INFINITY;
+        }
+      } else if (!MASKED && !full) {
         const v4i id0 = *(const v4i*)(sidx + c * kChunk + 4 * g);
         const v4i id1 = *(const v4i*)(sidx + c * kChunk + 16 + 4 * g);
 #pragma unroll
@@ -366,10 +404,12 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       }
       uint32_t pk[4];
       float psum = 0.0f;
+      float m_sub = m_use[ht];
+      if constexpr (MASKED) m_sub = m_sub == -INFINITY ? 0.0f : m_sub;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p0 = fast_exp2(fmaf(z[2 * i], a.scale_log2, -m_use[ht]));
-        const float p1 = fast_exp2(fmaf(z[2 * i + 1], a.scale_log2, -m_use[ht]));
+        const float p0 = fast_exp2(fmaf(z[2 * i], a.scale_log2, -m_sub));
+        const float p1 = fast_exp2(fmaf(z[2 * i + 1], a.scale_log2, -m_sub));
         psum += p0 + p1;
         pk[i] = pack_bf16x2(p0, p1);
       }
@@ -382,10 +422,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     __syncthreads();
 
     // the chunk before this one is done everywhere: reuse its buffer for the next gather
-    if (to_issue) {
-      issue(__builtin_ctzll(to_issue), (it + kStages - 1) % kStages);
-      to_issue &= to_issue - 1;
-    }
+    issue_next((it + kStages - 1) % kStages);
 
     // ---- O^T = alpha * O^T + V^T . P^T for this wave's d-range, all 128 heads
     float al8[kHeadTiles];
@@ -486,18 +523,20 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
-template <int DQK, int DV, int NW>
+template <int DQK, int DV, int NW, bool MASKED>
 hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
   using S = AttnShape<DQK, DV, NW>;
-  const int nch = (a.k + kChunk - 1) / kChunk;
+  // sparse: the staged indices; masked: one selection word per chunk of the row
+  const size_t tail = MASKED ? (size_t)((a.Lk + kChunk - 1) / kChunk) * sizeof(uint32_t)
+                             : (size_t)((a.k + kChunk - 1) / kChunk) * kChunk * sizeof(int32_t);
   const size_t smem = (size_t)kStages * S::CHUNK_BYTES + 2 * (size_t)S::P_BYTES +
-                      3 * 128 * sizeof(float) + (size_t)nch * kChunk * sizeof(int32_t);
+                      3 * 128 * sizeof(float) + tail;
   static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)sparse_mla_kernel<DQK, DV, NW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+      (const void*)sparse_mla_kernel<DQK, DV, NW, MASKED>, hipFuncAttributeMaxDynamicSharedMemorySize,
       160 * 1024);
   if (attr != hipSuccess) return attr;
   const long long rows = (long long)a.B * a.Lq;
-  const hipError_t e = launch_kernel((const void*)sparse_mla_kernel<DQK, DV, NW>,
+  const hipError_t e = launch_kernel((const void*)sparse_mla_kernel<DQK, DV, NW, MASKED>,
                                      dim3((unsigned)(rows * a.nsplit)), dim3(64 * NW), smem, stream, a);
   if (e != hipSuccess || a.nsplit == 1) return e;
   return launch_kernel((const void*)attn_combine_kernel, dim3((unsigned)(rows * a.H)), dim3(128), 0,
@@ -524,8 +563,15 @@ size_t attn_workspace_bytes(int rows, int k, int H, int Dv) {
 }
 
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream) {
-  if (a.Dv == 512 && a.Dr == 64) return launch_shape<576, 512, 8>(a, stream);
-  if (a.Dv == 64 && a.Dr == 16) return launch_shape<80, 64, 4>(a, stream);
+  if (a.Dv == 512 && a.Dr == 64) return launch_shape<576, 512, 8, false>(a, stream);
+  if (a.Dv == 64 && a.Dr == 16) return launch_shape<80, 64, 4, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_masked_mha_attn(const AttnArgs& a, hipStream_t stream) {
+  if (a.nsplit != 1) return hipErrorInvalidValue;
+  if (a.Dv == 512 && a.Dr == 64) return launch_shape<576, 512, 8, true>(a, stream);
+  if (a.Dv == 64 && a.Dr == 16) return launch_shape<80, 64, 4, true>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_forward",
-            "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
+    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_masked_mha_attn",
+            "dsa_forward", "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
     lib = ctypes.CDLL(dsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -93,6 +93,20 @@ def test_null_and_alignment():
     # a null problem pointer
     lib = dsa.lib
     assert lib.dsa_index_scores(None, FAKE, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_masked_mode_checks():
+    # the masked mode keeps one selection bit per key of the causal range in LDS
+    long = Problem(1, 4, 65537, 65533, 4, 32, 64, 8, 64, 16, 0.125)
+    s, msg = _status(dsa.dsa_masked_mha_attn, long, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert s == -3 and "65536" in msg
+    s, _ = _status(dsa.dsa_masked_mha_attn, GOOD, None, FAKE, FAKE, FAKE, stream=0)
+    assert s == -1
+    s, _ = _status(dsa.dsa_masked_mha_attn, GOOD, FAKE, FAKE, FAKE, FAKE + 4, stream=0)
+    assert s == -5
+    s, _ = _status(dsa.dsa_masked_mha_attn, Problem(**{**GOOD.__dict__, "d_latent": 128}),
+                   FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert s == -3
 
 
 def test_workspace_sizes_and_forward_checks():

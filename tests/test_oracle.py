@@ -362,6 +362,66 @@ def test_attention_value_is_latent_prefix_not_rope():
     assert not np.array_equal(o1, o3)
 
 
+# Masked mode for short prefill (dense causal softmax with a selection mask)
+
+def test_masked_mode_full_selection_is_dense_causal_sdpa():
+    """Selecting every token of the causal prefix leaves nothing masked: the
+    dense masked softmax is then dense causal attention (torch SDPA, float64)."""
+    rng = RNG(14)
+    L, H, Dv, Dr, k = 24, 4, 16, 8, 32
+    kv_, q_ = _attn_case(rng, L, H, Dv, Dr)
+    idx = np.array([list(range(t + 1)) + [-1] * (k - t - 1) for t in range(L)], np.int32)
+    scale = 1 / math.sqrt(Dv + Dr)
+    out, lse = oracle.masked_mha_attn(kv_, q_, idx, np.zeros(L, np.int32), np.arange(L, dtype=np.int32),
+                                      Dv, scale)
+    Q = torch.from_numpy(bf16_vals(q_)).permute(1, 0, 2)
+    K = torch.from_numpy(bf16_vals(kv_[0])).expand(H, L, Dv + Dr)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, K[..., :Dv], is_causal=True, scale=scale)
+    np.testing.assert_allclose(out, ref.permute(1, 0, 2).numpy(), rtol=0, atol=2e-6)
+    logits = (Q @ K.transpose(-1, -2)) * scale
+    ref_lse = torch.logsumexp(logits.masked_fill(torch.ones(L, L, dtype=torch.bool).triu(1), -math.inf),
+                              dim=-1).T
+    np.testing.assert_allclose(lse, ref_lse.numpy(), rtol=1e-6, atol=1e-6)
+
+
+def test_masked_mode_equals_sparse_on_topk_selections():
+    """On selections made by the top-k (distinct, at or before pos(t)) the dense
+    masked softmax and the sparse softmax over the selected latents are the same
+    attention, computed two ways."""
+    wl = dsa_inputs.WORKLOADS["tiny"]
+    rows = np.arange(wl.q_len)
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    qi = dsa_inputs.q_idx(wl).reshape(len(rows), wl.idx_heads, wl.idx_dim)
+    s = oracle.index_scores(dsa_inputs.k_idx(wl), qi, dsa_inputs.w(wl).reshape(len(rows), -1), rb, pos)
+    idx = oracle.topk(s, pos, wl.topk)
+    kv_ = dsa_inputs.kv(wl)
+    q_ = dsa_inputs.q(wl).reshape(len(rows), wl.heads, -1)
+    o1, l1 = oracle.sparse_mla_attn(kv_, q_, idx, rb, wl.d_latent, wl.softmax_scale)
+    o2, l2 = oracle.masked_mha_attn(kv_, q_, idx, rb, pos, wl.d_latent, wl.softmax_scale)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(l2, l1, rtol=1e-6, atol=1e-6)
+
+
+def test_masked_mode_ignores_repeats_late_and_invalid_entries():
+    rng = RNG(15)
+    L, H, Dv, Dr, k = 30, 2, 8, 8, 12
+    kv_, q_ = _attn_case(rng, L, H, Dv, Dr)
+    pos = np.array([20], np.int32)
+    sel = np.sort(rng.choice(21, size=6, replace=False)).astype(np.int32)
+    clean = np.concatenate([sel, [-1] * (k - 6)]).astype(np.int32)[None]
+    # the same tokens listed twice, plus entries past pos, past Lk and negative
+    noisy = np.concatenate([sel[::-1], sel[:3], [25, L + 3, -4]]).astype(np.int32)[None]
+    assert noisy.shape == (1, k)
+    rb = np.zeros(1, np.int32)
+    o1, l1 = oracle.sparse_mla_attn(kv_, q_[:1], clean, rb, Dv, 0.25)
+    o2, l2 = oracle.masked_mha_attn(kv_, q_[:1], noisy, rb, pos, Dv, 0.25)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(l2, l1, rtol=1e-6)
+    empty = np.full((1, k), -1, np.int32); empty[0, 0] = 25  # only a token past pos
+    oe, le = oracle.masked_mha_attn(kv_, q_[:1], empty, rb, pos, Dv, 0.25)
+    assert (oe == 0).all() and np.isneginf(le).all()
+
+
 # ---------------------------------------------------------------------------
 # Whole path on the tiny workload
 # ---------------------------------------------------------------------------
@@ -398,3 +458,4 @@ def test_workload_pair_counts_closed_form():
     assert c["decode1m"].selected_pairs() == 4 * 2048
     assert c["chunked1m"].causal_pairs() == sum(range(2 ** 20 - 4096 + 1, 2 ** 20 + 1))
     assert c["chunked1m"].selected_pairs() == 4096 * 2048
+    assert c["prefill2k"].selected_pairs() == c["prefill2k"].causal_pairs() == 2048 * 2049 // 2
