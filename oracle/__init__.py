@@ -59,6 +59,9 @@ def lib():
         L.dsa_oracle_masked_mha_attn.argtypes = [i32, i32, i32, i32, i32, f32, i64,
                                                  vp, vp, vp, vp, vp, vp, vp]
         L.dsa_oracle_masked_mha_attn.restype = None
+        L.dsa_oracle_sparse_mla_attn_bwd.argtypes = [i32, i32, i32, i32, i32, f32, i64,
+                                                     vp, vp, vp, vp, vp, vp, vp]
+        L.dsa_oracle_sparse_mla_attn_bwd.restype = None
         L.dsa_oracle_max_threads.argtypes = []
         L.dsa_oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -150,6 +153,34 @@ def sparse_mla_attn(kv, q_rows, indices, row_batch, d_latent: int, softmax_scale
     lib().dsa_oracle_sparse_mla_attn(Lk, H, d_latent, Dqk - d_latent, k, float(softmax_scale), R,
                                      rbp, qp, kv.ctypes.data, ip, out.ctypes.data, lse.ctypes.data)
     return out, lse
+
+
+def sparse_mla_attn_bwd(kv, q_rows, indices, row_batch, dout_rows, d_latent: int,
+                        softmax_scale: float, batch: int):
+    """Gradients of sparse_mla_attn over fixed indices, in double precision.
+
+    dout_rows [R, H, D_v] is the upstream gradient of the output.  Returns
+    (dq [R, H, D_v + D_r] float64, dkv [batch, Lk, D_v + D_r] float64), dkv
+    summed over the given rows only.  With o = sum_i p_i v_i: D = dout . o,
+    dz_i = p_i (dout . v_i - D), dq = scale sum_i dz_i kv_i,
+    dkv[s_i] += scale dz_i q + p_i dout (value columns)."""
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    B, Lk, Dqk = kv.shape
+    assert batch == B
+    q_rows, qp = _c(q_rows, np.uint16)
+    R, H, Dqk2 = q_rows.shape
+    assert Dqk2 == Dqk and 0 < d_latent <= Dqk
+    indices, ip = _c(indices, np.int32)
+    k = indices.shape[1]
+    rb, rbp = _c(row_batch, np.int32)
+    g, gp = _c(dout_rows, np.float64)
+    assert g.shape == (R, H, d_latent) and indices.shape[0] == R
+    dq = np.empty((R, H, Dqk), dtype=np.float64)
+    dkv = np.zeros((B, Lk, Dqk), dtype=np.float64)
+    lib().dsa_oracle_sparse_mla_attn_bwd(Lk, H, d_latent, Dqk - d_latent, k, float(softmax_scale), R,
+                                         rbp, qp, kv.ctypes.data, ip, gp, dq.ctypes.data,
+                                         dkv.ctypes.data)
+    return dq, dkv
 
 
 def masked_mha_attn(kv, q_rows, indices, row_batch, row_pos, d_latent: int, softmax_scale: float):

@@ -36,6 +36,15 @@
  *    written here as that dense masked softmax, separately from the sparse
  *    function above, so that the two formulations can be checked against
  *    each other.
+ *  - Backward of the sparse attention over fixed indices (the sparse training
+ *    stage trains every parameter with the selection on: DeepSeek-V3.2 spec
+ *    sheet, design overview; lightning-indexer post, section on training).
+ *    With o = sum_i p_i v_i and p = softmax(z), z_i = scale * q . kv_i, for an
+ *    upstream gradient dout of o: D = dout . o, dp_i = dout . v_i,
+ *    dz_i = p_i (dp_i - D); then dq = scale * sum_i dz_i kv_i and each listed
+ *    row gets dkv[s_i] += scale * dz_i q, plus p_i dout on its value columns.
+ *    Each index entry is one term, as in the forward.  The gradient does not
+ *    flow into the selection (the indices are fixed).
  *
  * Query rows are given explicitly (batch index, absolute position and the
  * row's own query data), so any subset of a workload's rows can be evaluated.
@@ -251,6 +260,88 @@ void dsa_oracle_masked_mha_attn(int32_t kv_len, int32_t heads, int32_t d_latent,
       free(acc);
     }
   }
+}
+
+/* Gradients of dsa_oracle_sparse_mla_attn for the given rows and upstream
+ * gradient dout [nrows, heads, d_latent]: dq [nrows, heads, dqk] (written) and
+ * dkv [batch, kv_len, dqk] (accumulated into; the caller zeroes it), in double
+ * precision.  Entries outside [0, kv_len) are skipped, as in the forward. */
+void dsa_oracle_sparse_mla_attn_bwd(int32_t kv_len, int32_t heads, int32_t d_latent, int32_t d_rope,
+                                    int32_t topk, float softmax_scale, int64_t nrows,
+                                    const int32_t* row_batch, const uint16_t* q_rows,
+                                    const uint16_t* kv, const int32_t* indices, const double* dout,
+                                    double* dq, double* dkv) {
+  const int32_t dqk = d_latent + d_rope;
+  const double scale = (double)softmax_scale;
+  double* pz = (double*)malloc((size_t)nrows * heads * topk * 2 * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+  for (int64_t r = 0; r < nrows; ++r) {
+    for (int32_t h = 0; h < heads; ++h) {
+      const uint16_t* cache = kv + (int64_t)row_batch[r] * kv_len * dqk;
+      const int32_t* sel = indices + r * topk;
+      const double* g = dout + (r * heads + h) * d_latent;
+      double* p = pz + ((r * heads + h) * topk) * 2;  /* p_i, dz_i interleaved */
+      double* qh = (double*)malloc((size_t)dqk * sizeof(double));
+      double* o = (double*)calloc((size_t)d_latent, sizeof(double));
+      for (int d = 0; d < dqk; ++d) qh[d] = bf16_to_double(q_rows[(r * heads + h) * dqk + d]);
+      /* forward: softmax over the listed entries */
+      double zmax = -INFINITY;
+      for (int i = 0; i < topk; ++i) {
+        const int32_t s = sel[i];
+        p[2 * i] = -INFINITY;
+        if (s < 0 || s >= kv_len) continue;
+        const uint16_t* row = cache + (int64_t)s * dqk;
+        double dot = 0.0;
+        for (int d = 0; d < dqk; ++d) dot += qh[d] * bf16_to_double(row[d]);
+        p[2 * i] = scale * dot;
+        if (p[2 * i] > zmax) zmax = p[2 * i];
+      }
+      double Z = 0.0;
+      for (int i = 0; i < topk; ++i)
+        if (p[2 * i] > -INFINITY) Z += exp(p[2 * i] - zmax);
+      for (int i = 0; i < topk; ++i) {
+        p[2 * i] = p[2 * i] > -INFINITY ? exp(p[2 * i] - zmax) / Z : 0.0;
+        p[2 * i + 1] = 0.0;
+        if (p[2 * i] == 0.0) continue;
+        const uint16_t* row = cache + (int64_t)sel[i] * dqk;
+        for (int d = 0; d < d_latent; ++d) o[d] += p[2 * i] * bf16_to_double(row[d]);
+      }
+      /* backward */
+      double D = 0.0;
+      for (int d = 0; d < d_latent; ++d) D += g[d] * o[d];
+      double* dqh = dq + (r * heads + h) * dqk;
+      for (int d = 0; d < dqk; ++d) dqh[d] = 0.0;
+      for (int i = 0; i < topk; ++i) {
+        const int32_t s = sel[i];
+        if (s < 0 || s >= kv_len) continue;
+        const uint16_t* row = cache + (int64_t)s * dqk;
+        double dp = 0.0;
+        for (int d = 0; d < d_latent; ++d) dp += g[d] * bf16_to_double(row[d]);
+        const double dz = p[2 * i] * (dp - D);
+        p[2 * i + 1] = dz;
+        for (int d = 0; d < dqk; ++d) dqh[d] += scale * dz * bf16_to_double(row[d]);
+      }
+      free(qh);
+      free(o);
+    }
+  }
+  /* dkv: rows may list the same token, so the scatter runs in order */
+  for (int64_t r = 0; r < nrows; ++r)
+    for (int32_t h = 0; h < heads; ++h) {
+      const int32_t* sel = indices + r * topk;
+      const double* g = dout + (r * heads + h) * d_latent;
+      const double* p = pz + ((r * heads + h) * topk) * 2;
+      for (int i = 0; i < topk; ++i) {
+        const int32_t s = sel[i];
+        if (s < 0 || s >= kv_len) continue;
+        double* dst = dkv + ((int64_t)row_batch[r] * kv_len + s) * dqk;
+        for (int d = 0; d < dqk; ++d) {
+          const double qd = bf16_to_double(q_rows[(r * heads + h) * dqk + d]);
+          dst[d] += scale * p[2 * i + 1] * qd + (d < d_latent ? p[2 * i] * g[d] : 0.0);
+        }
+      }
+    }
+  free(pz);
 }
 
 int dsa_oracle_max_threads(void) {

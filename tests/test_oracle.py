@@ -422,6 +422,72 @@ def test_masked_mode_ignores_repeats_late_and_invalid_entries():
     assert (oe == 0).all() and np.isneginf(le).all()
 
 
+# Backward of the sparse attention over fixed indices
+
+def _fwd_loss(qv, kvv, idx, g, Dv, scale):
+    """sum(dout * out) of the forward definition, in float64 (for finite
+    differences): per row and head, softmax over the listed entries."""
+    R, H, _ = qv.shape
+    tot = 0.0
+    for r in range(R):
+        sel = [s for s in idx[r] if 0 <= s < kvv.shape[0]]
+        if not sel:
+            continue
+        K = kvv[sel]                                  # [n, Dqk]
+        z = scale * (qv[r] @ K.T)                     # [H, n]
+        z = z - z.max(1, keepdims=True)
+        p = np.exp(z); p /= p.sum(1, keepdims=True)
+        tot += float((g[r] * (p @ K[:, :Dv])).sum())
+    return tot
+
+
+def test_attention_backward_matches_finite_differences():
+    """The analytic gradients against central differences of the forward
+    definition (every q entry and every kv entry of a small case, with a
+    repeated index and an invalid one)."""
+    rng = RNG(16)
+    L, H, Dv, Dr, k, R = 12, 3, 4, 4, 6, 3
+    kv_ = bf16_bits(rng.normal(size=(1, L, Dv + Dr)))
+    q_ = bf16_bits(rng.normal(size=(R, H, Dv + Dr)))
+    idx = np.array([[0, 3, 5, 7, -1, 11], [2, 2, 9, 4, 1, 6], [10, 8, 0, 1, 5, L + 2]], np.int32)
+    g = rng.normal(size=(R, H, Dv))
+    scale = 0.7
+    dq, dkv = oracle.sparse_mla_attn_bwd(kv_, q_, idx, np.zeros(R, np.int32), g, Dv, scale, 1)
+    qv, kvv = bf16_vals(q_).astype(np.float64), bf16_vals(kv_[0]).astype(np.float64)
+    eps = 1e-6
+    num_q = np.zeros_like(qv)
+    for i in np.ndindex(qv.shape):
+        a = qv.copy(); a[i] += eps
+        b = qv.copy(); b[i] -= eps
+        num_q[i] = (_fwd_loss(a, kvv, idx, g, Dv, scale) - _fwd_loss(b, kvv, idx, g, Dv, scale)) / (2 * eps)
+    num_kv = np.zeros_like(kvv)
+    for i in np.ndindex(kvv.shape):
+        a = kvv.copy(); a[i] += eps
+        b = kvv.copy(); b[i] -= eps
+        num_kv[i] = (_fwd_loss(qv, a, idx, g, Dv, scale) - _fwd_loss(qv, b, idx, g, Dv, scale)) / (2 * eps)
+    np.testing.assert_allclose(dq, num_q, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(dkv[0], num_kv, rtol=1e-6, atol=1e-8)
+    assert (dkv[0, [s for s in range(L) if s not in idx]] == 0).all()  # unlisted rows get nothing
+
+
+def test_attention_backward_closed_forms():
+    rng = RNG(17)
+    L, H, Dv, Dr, k = 10, 2, 4, 4, 5
+    kv_ = bf16_bits(rng.normal(size=(1, L, Dv + Dr)))
+    q_ = bf16_bits(rng.normal(size=(2, H, Dv + Dr)))
+    g = rng.normal(size=(2, H, Dv))
+    # one selected token: p = 1, so dz = 0: dq = 0 and dkv = dout on the value columns
+    one = np.array([[4, -1, -1, -1, -1], [4, -1, -1, -1, -1]], np.int32)
+    dq, dkv = oracle.sparse_mla_attn_bwd(kv_, q_, one, np.zeros(2, np.int32), g, Dv, 0.5, 1)
+    assert (dq == 0).all()
+    np.testing.assert_allclose(dkv[0, 4, :Dv], g.sum((0, 1)), rtol=1e-12)
+    assert (dkv[0, 4, Dv:] == 0).all()
+    # sum_i dz_i = 0: the rope columns (which only the scores reach) sum to zero over the keys
+    idx = np.stack([rng.choice(L, size=k, replace=False) for _ in range(2)]).astype(np.int32)
+    _, dkv = oracle.sparse_mla_attn_bwd(kv_, q_, idx, np.zeros(2, np.int32), g, Dv, 0.5, 1)
+    np.testing.assert_allclose(dkv[0, :, Dv:].sum(0), 0.0, atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # Whole path on the tiny workload
 # ---------------------------------------------------------------------------
