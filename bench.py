@@ -13,6 +13,10 @@ CPU oracle timed on a bounded row sample of the same workload.
 --attn masked replaces the sparse attention by dsa_masked_mha_attn (the masked
 mode for short prefill: dense over each query's causal range, non-selected
 tokens masked); its roofline counts that dense work.
+
+--bwd times the backward of the sparse attention over fixed indices
+(dsa_sparse_mla_attn_bwd: dq and dkv for an upstream gradient of the output)
+instead; the indices, output and lse come from one untimed forward pass.
 """
 from __future__ import annotations
 
@@ -47,6 +51,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the attention backward over fixed indices instead of the forward step")
     ap.add_argument("--attn", choices=["sparse", "masked"], default="sparse",
                     help="attention stage: the sparse kernel, or the masked mode for short prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -87,6 +93,75 @@ def algorithmic(wl):
             bytes=rows * wl.heads * (2 * wl.d_qk + 4 * wl.d_latent + 4) + 4.0 * rows * wl.topk
             + 2.0 * wl.d_qk * causal),
     }
+
+
+def bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws, ws_bytes, aws, aws_bytes,
+              q_idx, k_idx, w):
+    """Backward of the sparse attention: one untimed forward for the indices,
+    output and lse, then `steps` timed calls of dsa_sparse_mla_attn_bwd."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
+    dsa.dsa_topk(prob, scores, indices, ws, ws_bytes, stream=stream)
+    dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
+    torch.cuda.synchronize()
+    del scores
+    torch.cuda.empty_cache()
+    rows = wl.batch * wl.q_len
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    dout = torch.randn((wl.batch, wl.q_len, wl.heads, wl.d_latent), dtype=torch.float32, device="cuda",
+                       generator=gen)
+    dq = torch.empty((wl.batch, wl.q_len, wl.heads, wl.d_qk), dtype=torch.float32, device="cuda")
+    dkv = torch.zeros((wl.batch, wl.kv_len, wl.d_qk), dtype=torch.float32, device="cuda")
+    bws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD)
+    bws = torch.empty(bws_bytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsa.dsa_sparse_mla_attn_bwd(prob, q, kv, indices, out, lse, dout, dq, dkv, bws, bws_bytes,
+                                    stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in ev:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [a.elapsed_time(b) for a, b in ev]
+    sel = wl.selected_pairs()
+    # per (selected pair, head): scores 2*Dqk, dout.v 2*Dv, dq 2*Dqk, dkv 2*Dqk + 2*Dv
+    flop = 2.0 * wl.heads * sel * (3 * wl.d_qk + 2 * wl.d_latent)
+    avg = float(np.mean(ms))
+    tf = flop / (avg * 1e-3) / 1e12
+    result = {
+        "metric": "DSA sparse attention backward query tokens/s",
+        "value": rows * args.steps / wall,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "event_ms_per_step": avg,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.batch, "q_len": wl.q_len, "kv_len": wl.kv_len,
+                   "topk": wl.topk, "heads": wl.heads, "d_latent": wl.d_latent, "d_rope": wl.d_rope,
+                   "pass": "attention backward"},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "kernel": "sparse_mla_attn_bwd", "traffic": None},
+        "algorithmic_flop": flop,
+        "workspace_bytes": bws_bytes,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result))
 
 
 def traffic_for(kernel: str):
@@ -174,6 +249,11 @@ def main():
     aws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
     aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+
+    if args.bwd:
+        bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws, ws_bytes, aws,
+                  aws_bytes, q_idx, k_idx, w)
+        return
 
     attn_name = "sparse_mla_attn" if args.attn == "sparse" else "masked_mha_attn"
     names = ["index_scores", "topk", attn_name]

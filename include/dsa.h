@@ -18,6 +18,8 @@
  *                        head, one selection per query position (lightning
  *                        indexer post, same section; spec sheet, "Inference
  *                        efficiency" table, KV-cache design).
+ *   dsa_sparse_mla_attn_bwd  gradients of the sparse attention (dq, dkv) over
+ *                        fixed indices, for the sparse training stage.
  *   dsa_masked_mha_attn  the same attention computed densely over each
  *                        query's causal range with the non-selected tokens
  *                        masked: the masked mode for short prefill.
@@ -82,7 +84,13 @@ typedef struct dsa_problem {
 } dsa_problem;
 
 /* Operation selector for dsa_workspace_size(). */
-enum dsa_op { DSA_OP_INDEX_SCORES = 0, DSA_OP_TOPK = 1, DSA_OP_SPARSE_MLA_ATTN = 2, DSA_OP_FORWARD = 3 };
+enum dsa_op {
+  DSA_OP_INDEX_SCORES = 0,
+  DSA_OP_TOPK = 1,
+  DSA_OP_SPARSE_MLA_ATTN = 2,
+  DSA_OP_FORWARD = 3,
+  DSA_OP_SPARSE_MLA_ATTN_BWD = 4
+};
 
 /*
  * Lightning indexer scores.
@@ -156,6 +164,38 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
 int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
                         const int32_t* indices, float* out, float* lse, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of dsa_sparse_mla_attn over fixed indices: the gradients the sparse
+ * training stage needs, where every parameter is trained with the selection
+ * on (DeepSeek-V3.2 spec sheet, design overview; lightning-indexer post,
+ * training section).  No gradient flows into the indices.  Per (b, t, h),
+ * with z_i, p = softmax(z) and o as in the forward and g = dout[b,t,h,:]:
+ *   D = g . o,  dz_i = p_i (g . v_i - D),
+ *   dq[b,t,h,:]  = softmax_scale * sum_i dz_i kv[b,s_i,:]
+ *   dkv[b,s_i,:] += softmax_scale * dz_i q[b,t,h,:]   (+ p_i g on the first D_v columns)
+ * summed over every (t, h, i) that lists s_i (entries outside [0, Lk) are
+ * skipped, a repeated entry is a separate term, as in the forward).
+ *
+ *   q, kv, indices  as for dsa_sparse_mla_attn
+ *   out  [B, Lq, H, D_v]  float32, the forward's output
+ *   lse  [B, Lq, H]       float32, the forward's lse (required)
+ *   dout [B, Lq, H, D_v]  float32, the upstream gradient
+ *   dq   [B, Lq, H, D_qk] float32 output (written)
+ *   dkv  [B, Lk, D_qk]    float32, ACCUMULATED into with atomic adds: the
+ *                         caller zeroes it (or holds gradients to add to);
+ *                         the summation order, hence the last bits, varies
+ *                         from run to run
+ *   workspace: at least dsa_workspace_size(p, DSA_OP_SPARSE_MLA_ATTN_BWD)
+ *              bytes, 16-byte aligned (3 * B*Lq * k * 256 bytes: P and dZ in
+ *              bf16); contents on return are unspecified.
+ * The products run on bf16 matrix cores with fp32 accumulation; dout, P and
+ * dZ are rounded to bf16 for them.  dq and dkv must not alias any input.
+ */
+int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                            const int32_t* indices, const float* out, const float* lse,
+                            const float* dout, float* dq, float* dkv, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Masked mode for short prefill: the same attention as dsa_sparse_mla_attn,

@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_OP_INDEX_SCORES, DSA_OP_TOPK, DSA_OP_SPARSE_MLA_ATTN, DSA_OP_FORWARD = 0, 1, 2, 3
+DSA_OP_SPARSE_MLA_ATTN_BWD = 4
 STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_UNSUPPORTED",
           -4: "DSA_ERR_WORKSPACE", -5: "DSA_ERR_ALIGN", -6: "DSA_ERR_HIP"}
 
@@ -78,9 +79,10 @@ def _load():
     L.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.dsa_sparse_mla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_masked_mha_attn,
-              L.dsa_forward):
+              L.dsa_sparse_mla_attn_bwd, L.dsa_forward):
         f.restype = i32
     L.dsa_workspace_size.argtypes = [P, i32]
     L.dsa_workspace_size.restype = sz
@@ -147,6 +149,17 @@ def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, workspa
     _check(lib.dsa_sparse_mla_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
                                    _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
                                    _stream(stream)))
+
+
+def dsa_sparse_mla_attn_bwd(problem: Problem, q, kv, indices, out, lse, dout, dq, dkv,
+                            workspace, workspace_bytes: int = 0, stream=None) -> None:
+    """dq (written) and dkv (accumulated into) of the sparse attention over fixed
+    indices (include/dsa.h: dsa_sparse_mla_attn_bwd)."""
+    if workspace is not None and not isinstance(workspace, int) and workspace_bytes == 0:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_mla_attn_bwd(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
+                                       _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv),
+                                       _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def dsa_masked_mha_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:

@@ -166,6 +166,8 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       return dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
     case DSA_OP_SPARSE_MLA_ATTN:
       return check_attn(p) ? bad : attn_ws_bytes(p);
+    case DSA_OP_SPARSE_MLA_ATTN_BWD:
+      return check_attn(p) ? bad : dsa::attn_bwd_workspace_bytes(p->batch * p->q_len, p->topk);
     case DSA_OP_FORWARD:
       if (check_index(p) || check_attn(p)) return bad;
       return round_up(scores_bytes(p)) + round_up(indices_bytes(p)) +
@@ -221,6 +223,40 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
                         attn_args(p, q, kv, indices, out, lse, workspace, workspace_bytes),
                         (hipStream_t)stream),
                     "sparse_mla_attn launch");
+}
+
+int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                            const int32_t* indices, const float* out, const float* lse,
+                            const float* dout, float* dq, float* dkv, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_attn(p)) return s;
+  if (int s = check_ptr(q, "q", 16)) return s;
+  if (int s = check_ptr(kv, "kv", 16)) return s;
+  if (int s = check_ptr(indices, "indices", 16)) return s;
+  if (int s = check_ptr(out, "out", 16)) return s;
+  if (int s = check_ptr(lse, "lse", 4)) return s;
+  if (int s = check_ptr(dout, "dout", 16)) return s;
+  if (int s = check_ptr(dq, "dq", 16)) return s;
+  if (int s = check_ptr(dkv, "dkv", 16)) return s;
+  const long long rows = (long long)p->batch * p->q_len;
+  const size_t need = dsa::attn_bwd_workspace_bytes((int)rows, p->topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "sparse_mla_attn_bwd needs %zu workspace bytes, got %zu", need,
+                workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  dsa::AttnBwdArgs a{};
+  a.q = q; a.kv = kv; a.indices = indices; a.out = out; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dkv = dkv;
+  const size_t part = need / 3 / sizeof(uint16_t);  // [rows, kpad, 128] bf16 each
+  a.ws_dzf = (uint16_t*)workspace;
+  a.ws_pk = a.ws_dzf + part;
+  a.ws_dzk = a.ws_pk + part;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.H = p->heads;
+  a.Dv = p->d_latent; a.Dr = p->d_rope; a.k = p->topk;
+  a.scale = p->softmax_scale;
+  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  return hip_status(dsa::launch_sparse_mla_attn_bwd(a, (hipStream_t)stream), "sparse_mla_attn_bwd launch");
 }
 
 int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,

@@ -45,6 +45,25 @@ struct AttnArgs {
   float* part_lse;
 };
 
+// Backward of the sparse attention over fixed indices.
+struct AttnBwdArgs {
+  const uint16_t* q;        // [B, Lq, H, Dqk] bf16
+  const uint16_t* kv;       // [B, Lk, Dqk]    bf16
+  const int32_t* indices;   // [B, Lq, k]
+  const float* out;         // [B, Lq, H, Dv]  forward output
+  const float* lse;         // [B, Lq, H]      forward log-sum-exp (natural log)
+  const float* dout;        // [B, Lq, H, Dv]  upstream gradient
+  float* dq;                // [B, Lq, H, Dqk] written
+  float* dkv;               // [B, Lk, Dqk]    accumulated into
+  // workspace: dZ in operand order, P and dZ key-major ([B*Lq, kpad, 128] bf16)
+  uint16_t* ws_dzf;
+  uint16_t* ws_pk;
+  uint16_t* ws_dzk;
+  int B, Lq, Lk, H, Dv, Dr, k;
+  float scale;              // softmax_scale
+  float scale_log2;         // softmax_scale * log2(e)
+};
+
 // Launch `kernel(arg)` and return the launch's own status (not the thread's
 // sticky last-error state, which other libraries in the process also write).
 template <typename Arg>
@@ -64,6 +83,8 @@ hipError_t launch_masked_mha_attn(const AttnArgs& a, hipStream_t stream);
 // Parts per row when few rows would leave most CUs idle (1: no split), and the
 // workspace the split needs.
 int attn_splits(int rows, int k);
+hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
+size_t attn_bwd_workspace_bytes(int rows, int k);
 size_t attn_workspace_bytes(int rows, int k, int H, int Dv);
 
 }  // namespace dsa

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_symbols_exported():
     names = declared_functions()
     assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_masked_mha_attn",
-            "dsa_forward", "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
+            "dsa_sparse_mla_attn_bwd", "dsa_forward", "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
     lib = ctypes.CDLL(dsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
@@ -107,6 +107,38 @@ def test_masked_mode_checks():
     s, _ = _status(dsa.dsa_masked_mha_attn, Problem(**{**GOOD.__dict__, "d_latent": 128}),
                    FAKE, FAKE, FAKE, FAKE, stream=0)
     assert s == -3
+
+
+def test_backward_checks():
+    # P and dZ of every (row, selected entry, head) in bf16, three copies
+    # (operand order for dq, key-major for dkv), entries padded to 32, heads to 128
+    assert dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == 3 * 256 * 64 * 128 * 2
+    assert dsa.workspace_size(MLA, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == 3 * 4096 * 2048 * 128 * 2
+    odd = Problem(**{**GOOD.__dict__, "topk": 65})
+    assert dsa.workspace_size(odd, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == 3 * 256 * 96 * 128 * 2
+    need = dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD)
+    args = [FAKE] * 8
+    s, msg = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, FAKE, need - 1, stream=0)
+    assert s == -4 and str(need) in msg
+    s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, None, need, stream=0)
+    assert s == -4
+    s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, FAKE + 8, need, stream=0)
+    assert s == -5
+    for i, name in enumerate(["q", "kv", "indices", "out", "lse", "dout", "dq", "dkv"]):
+        a = list(args)
+        a[i] = None
+        s, msg = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *a, FAKE, need, stream=0)
+        assert s == -1 and name in msg, msg
+    a = list(args)
+    a[7] = FAKE + 4  # dkv
+    s, msg = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *a, FAKE, need, stream=0)
+    assert s == -5 and "dkv" in msg
+    s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, Problem(**{**GOOD.__dict__, "heads": 129}),
+                   *args, FAKE, 1 << 40, stream=0)
+    assert s == -3
+    s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, Problem(**{**GOOD.__dict__, "softmax_scale": 0.0}),
+                   *args, FAKE, need, stream=0)
+    assert s == -2
 
 
 def test_workspace_sizes_and_forward_checks():

@@ -1,0 +1,109 @@
+"""GPU parity of the sparse attention's backward over fixed indices (dq written,
+dkv accumulated) against the CPU oracle's double-precision gradients.
+
+Bar: max-abs error <= TOL * max|reference| per output.  dout, P and dZ are
+rounded to bf16 for the matrix cores (relative 2^-9 each) and the sums run in
+fp32, so the expected relative error is a few 1e-3; TOL = 2e-2 leaves room for
+the accumulation over 2048 entries."""
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs
+import oracle
+from gpu_util import Inputs, dev, log, run_stages
+from test_gpu_parity import EDGE
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_02_amd as m
+    return m
+
+
+def _bwd(dsa, prob, wl, d, indices, out, lse, dout):
+    dq = torch.full((wl.batch, wl.q_len, wl.heads, wl.d_qk), float("nan"), dtype=torch.float32, device="cuda")
+    dkv = torch.zeros((wl.batch, wl.kv_len, wl.d_qk), dtype=torch.float32, device="cuda")
+    nbytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dsa.dsa_sparse_mla_attn_bwd(prob, d["q"], d["kv"], indices, out, lse, dout, dq, dkv, ws)
+    torch.cuda.synchronize()
+    return dq, dkv
+
+
+def _check(label, got, ref):
+    err = float(np.abs(got - ref).max())
+    scale = float(np.abs(ref).max())
+    log(f"[{label}] max-abs {err:.3e} of max|ref| {scale:.3e} (relative {err / max(scale, 1e-30):.2e})")
+    assert err <= TOL * scale + 1e-6, f"{label}: {err} > {TOL} * {scale}"
+
+
+def _run_case(dsa, wl, rows_with_grad=None, indices_np=None, seed=0):
+    inp = Inputs.make(wl)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
+    _, indices, out, lse = run_stages(prob, d, wl)
+    if indices_np is not None:
+        indices = dev(indices_np.reshape(wl.batch, wl.q_len, wl.topk))
+        aws_b = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
+        aws = torch.empty(max(aws_b, 1), dtype=torch.uint8, device="cuda")
+        dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], indices, out, lse, aws, aws_b)
+        torch.cuda.synchronize()
+    R = wl.batch * wl.q_len
+    rng = np.random.default_rng(seed)
+    g = rng.normal(size=(R, wl.heads, wl.d_latent)).astype(np.float32)
+    rows = np.arange(R) if rows_with_grad is None else np.asarray(rows_with_grad)
+    mask = np.zeros(R, bool); mask[rows] = True
+    g[~mask] = 0.0
+    dout = dev(g.reshape(wl.batch, wl.q_len, wl.heads, wl.d_latent))
+    dq, dkv = _bwd(dsa, prob, wl, d, indices, out, lse, dout)
+    idx_np = indices.reshape(R, wl.topk).cpu().numpy()
+    rb, _ = dsa_inputs.row_batch_pos(wl, rows)
+    q_rows = inp.q.reshape(R, wl.heads, -1)[rows]
+    dq_or, dkv_or = oracle.sparse_mla_attn_bwd(inp.kv, q_rows, idx_np[rows], rb, g[rows].astype(np.float64),
+                                               wl.d_latent, wl.softmax_scale, wl.batch)
+    dq_gpu = dq.reshape(R, wl.heads, -1).cpu().numpy()
+    _check(f"{wl.name} dq", dq_gpu[rows], dq_or)
+    if rows_with_grad is not None:
+        assert (dq_gpu[~mask] == 0).all(), "rows without gradient must get dq = 0"
+    _check(f"{wl.name} dkv", dkv.cpu().numpy(), dkv_or)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "mla_small", "k_above_len"])
+def test_bwd_matches_oracle(dsa, name):
+    wl = dsa_inputs.WORKLOADS[name] if name in dsa_inputs.WORKLOADS else EDGE[name]
+    log(f"[{name}] B={wl.batch} Lq={wl.q_len} Lk={wl.kv_len} k={wl.topk} H={wl.heads} "
+        f"Dv={wl.d_latent}+{wl.d_rope}")
+    _run_case(dsa, wl)
+
+
+def test_bwd_invalid_repeated_and_empty_entries(dsa):
+    """Hand-built selections: -1 and out-of-range entries, a repeated token (a
+    separate term, as in the forward) and a row with nothing selected."""
+    wl = dsa_inputs.Workload("bwdhand", 22, 1, 8, 300, 292, 4, 32, 48, 16, 64, 16)
+    rng = np.random.default_rng(9)
+    R = wl.q_len
+    idx = np.full((R, wl.topk), -1, np.int32)
+    for r in range(R):
+        p = wl.q_start + r
+        if r == 3:
+            continue  # nothing selected
+        sel = rng.choice(p + 1, size=30, replace=False).astype(np.int32)
+        if r == 5:
+            sel[4] = sel[0]               # a repeated token
+            sel[7] = wl.kv_len + 11       # out of range
+        idx[r, :30] = sel
+    _run_case(dsa, wl, indices_np=idx)
+
+
+def test_bwd_prefill4k_sampled_rows(dsa):
+    """The 4K prefill at full size: the upstream gradient is non-zero on sampled
+    rows only, so dq elsewhere is 0 and dkv is exactly those rows' sum."""
+    wl = dsa_inputs.WORKLOADS["prefill4k"]
+    _run_case(dsa, wl, rows_with_grad=[0, 1, 2047, 2048, 3500, 4095], seed=3)
