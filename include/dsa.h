@@ -182,15 +182,22 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
  *   lse  [B, Lq, H]       float32, the forward's lse (required)
  *   dout [B, Lq, H, D_v]  float32, the upstream gradient
  *   dq   [B, Lq, H, D_qk] float32 output (written)
- *   dkv  [B, Lk, D_qk]    float32, ACCUMULATED into with atomic adds: the
- *                         caller zeroes it (or holds gradients to add to);
- *                         the summation order, hence the last bits, varies
- *                         from run to run
+ *   dkv  [B, Lk, D_qk]    float32, ACCUMULATED into: each listed token's
+ *                         total is added once (no atomics on dkv), so the
+ *                         caller zeroes it or passes gradients to add to;
+ *                         the order in which a token's terms are summed
+ *                         varies, hence its last bits may vary between runs
  *   workspace: at least dsa_workspace_size(p, DSA_OP_SPARSE_MLA_ATTN_BWD)
- *              bytes, 16-byte aligned (3 * B*Lq * k * 256 bytes: P and dZ in
- *              bf16); contents on return are unspecified.
- * The products run on bf16 matrix cores with fp32 accumulation; dout, P and
- * dZ are rounded to bf16 for them.  dq and dkv must not alias any input.
+ *              bytes, 256-byte aligned; contents on return are unspecified.
+ *              With R = B*Lq and kp = k rounded up to 32, it holds P and dZ
+ *              (3 * R*kp*128 bf16), one partial dkv row per (row, entry)
+ *              (R*kp*D_qk bf16) and the per-token lists of those entries
+ *              (R*k + 3*B*Lk int32, plus one int32 per 4096 tokens), each
+ *              part rounded up to 256 bytes.
+ * Requires B*Lq*kp and B*Lk below 2^31 (DSA_ERR_UNSUPPORTED otherwise).
+ * The products run on bf16 matrix cores with fp32 accumulation; dout, P, dZ
+ * and the partial dkv rows are rounded to bf16.  dq and dkv must not alias
+ * any input.
  */
 int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
                             const int32_t* indices, const float* out, const float* lse,

@@ -12,19 +12,22 @@
 //   dq = scale * sum_i dz_i kv_i,
 //   dkv[s_i] += scale * dz_i q  (+ p_i dout on the value columns).
 //
-// Three kernels, because dq contracts over the keys and dkv over the heads:
+// dq contracts over the keys and dkv over the heads, hence separate kernels:
 //  1. scores (one wave per 16 heads, 64 heads per block): the
 //     selected latent rows are gathered into LDS in chunks of 32; S^T = K.Q^T
 //     and dP^T = V.dO^T run on bf16 MFMA sharing each K fragment read; P comes
 //     straight from the forward's lse, dZ = P (dP - D).  P and dZ go to the
 //     workspace in bf16, dZ once in the MFMA operand order of kernel 2 and
-//     both once key-major for kernel 3.
+//     both once key-major (dZ times scale) for kernel 3.
 //  2. dq (one block per row): dQ^T = K^T.dZ^T per chunk with the transposing
 //     K reads of the forward's value product; wave w owns d-tiles w, w+NW, ...
-//  3. dkv (one block per row and 64 columns): per 32-key chunk,
-//     scale * dZ.Q + P.dO over the 128 heads on bf16 MFMA with Q and dO held
-//     in registers for the whole row, then one fp32 atomic add per element of
-//     the chunk's rows (rows are shared between queries).
+//  3. dkv: per row, the partial product scale * dZ.Q + P.dO of every slot
+//     over the 128 heads on bf16 MFMA (one block per row, Q and dO held in
+//     registers), stored in bf16; per key, the sum over the (row, slot) pairs
+//     that list it (inverted lists built by count / scan / fill kernels), added
+//     into dkv by one wave per key.
+#include <algorithm>
+
 #include "dsa_common.h"
 #include "launch.h"
 
@@ -277,7 +280,7 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
       const v4i zf = {(int)pack_bf16x2(zv[0], zv[1]), (int)pack_bf16x2(zv[2], zv[3]),
                       (int)pack_bf16x2(zv[4], zv[5]), (int)pack_bf16x2(zv[6], zv[7])};
       *(v4i*)(a.ws_dzf + ((((size_t)row * nch + c) * kBTiles + tile) * 64 + lane) * 8) = zf;
-      // P and dZ key-major [row][slot][128 heads] for the dkv kernel
+      // P and scale * dZ key-major [row][slot][128 heads] for the dkv products
       const int ln = opaque_tid() & 63;
       const size_t kmbase = ((size_t)row * kpad + (size_t)c * kBChunk + 4 * (ln >> 4)) * kBHeads +
                             16 * tile + (ln & 15);
@@ -285,7 +288,7 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
       for (int e = 0; e < 8; ++e) {
         const size_t o = kmbase + (size_t)(16 * (e >> 2) + (e & 3)) * kBHeads;
         a.ws_pk[o] = (uint16_t)(pack_bf16x2(pv[e], 0.0f) & 0xFFFFu);
-        a.ws_dzk[o] = (uint16_t)(pack_bf16x2(zv[e], 0.0f) & 0xFFFFu);
+        a.ws_dzk[o] = (uint16_t)(pack_bf16x2(zv[e] * a.scale, 0.0f) & 0xFFFFu);
       }
     }
     // the next chunk's copies are complete and every wave is done with this one
@@ -394,79 +397,347 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(AttnBwdArgs a) {
   }
 }
 
-// ---- 3. dkv[s] += scale * sum_h dZ[s,h] q[h] + sum_h P[s,h] dout[h]
-// Block (row, slice of 64 columns); wave w owns d-tile 4 * slice + w.
-template <int DQK, int DV>
-__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnBwdArgs a) {
-  constexpr int DQKP = (DQK + 31) / 32 * 32;
-  constexpr int NDT = DQKP / 16;
+// ---- 3. dkv[s] += sum over the (row, slot) pairs listing s of
+//         scale * dZ[slot,:] . Q + P[slot,:] . dO        (contracted over heads)
+// Fp32 atomics into dkv run at about one element per L2 channel and clock,
+// far below the rate the partial products are made at, so the reduction goes
+// through memory instead: every (row, slot) product is stored once in bf16,
+// the pairs are listed per key (count, scan, fill), and one wave per key sums
+// its list in fp32 and adds the total into dkv.  Each key is written by one
+// wave only; the order of a list depends on the fill's atomics, so the last
+// bits of dkv may vary from run to run.
+
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = 16;
+constexpr int kScanBlock = kScanThreads * kScanPer;  // keys per block of the scan
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(int32_t* p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 0;
+}
+
+// number of valid entries per key (b, s)
+__global__ __launch_bounds__(256) void bwd_count_kernel(AttnBwdArgs a) {
+  const long long total = (long long)a.B * a.Lq * a.k;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int s = a.indices[i];
+  if (s < 0 || s >= a.Lk) return;
+  const int b = (int)(i / ((long long)a.Lq * a.k));
+  atomicAdd(a.ws_cnt + (size_t)b * a.Lk + s, 1);
+}
+
+// exclusive scan of NT values over the block; `total` gets the block sum
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* lds, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = lds[w];
+    before += w < wave ? t : 0;
+    sum += t;
+  }
+  __syncthreads();
+  total = sum;
+  return before + x - v;
+}
+
+// per block of kScanBlock keys: the sum of its counts
+__global__ __launch_bounds__(kScanThreads) void bwd_scan_sums_kernel(const int32_t* cnt, int32_t* bsum, long long n) {
+  __shared__ int lds[kScanThreads / 64];
+  const long long base = (long long)blockIdx.x * kScanBlock + (long long)threadIdx.x * kScanPer;
+  int v = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) v += base + j < n ? cnt[base + j] : 0;
+  int total;
+  block_exclusive_scan<kScanThreads>(v, lds, total);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = total;
+}
+
+// exclusive scan of the block sums in place (one block)
+__global__ __launch_bounds__(1024) void bwd_scan_top_kernel(int32_t* bsum, int nb) {
+  __shared__ int lds[16];
+  int carry = 0;
+  for (int base = 0; base < nb; base += 1024) {
+    const int i = base + (int)threadIdx.x;
+    const int v = i < nb ? bsum[i] : 0;
+    int total;
+    const int ex = block_exclusive_scan<1024>(v, lds, total);
+    if (i < nb) bsum[i] = carry + ex;
+    carry += total;
+  }
+}
+
+// list offsets of the keys: off = cur = exclusive scan of the counts
+__global__ __launch_bounds__(kScanThreads) void bwd_scan_apply_kernel(AttnBwdArgs a, long long n) {
+  __shared__ int lds[kScanThreads / 64];
+  const long long base = (long long)blockIdx.x * kScanBlock + (long long)threadIdx.x * kScanPer;
+  int c[kScanPer];
+  int v = 0;
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    c[j] = base + j < n ? a.ws_cnt[base + j] : 0;
+    v += c[j];
+  }
+  int total;
+  int run = block_exclusive_scan<kScanThreads>(v, lds, total) + a.ws_bsum[blockIdx.x];
+#pragma unroll
+  for (int j = 0; j < kScanPer; ++j) {
+    if (base + j < n) {
+      a.ws_off[base + j] = run;
+      a.ws_cur[base + j] = run;
+    }
+    run += c[j];
+  }
+}
+
+// place every valid (row, slot) in its key's list as row * kpad + slot
+__global__ __launch_bounds__(256) void bwd_fill_kernel(AttnBwdArgs a) {
+  const long long total = (long long)a.B * a.Lq * a.k;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int s = a.indices[i];
+  if (s < 0 || s >= a.Lk) return;
+  const long long row = i / a.k;
+  const int slot = (int)(i - row * a.k);
+  const int b = (int)(row / a.Lq);
+  const int kpad = (a.k + kBChunk - 1) / kBChunk * kBChunk;
+  const int p = atomicAdd(a.ws_cur + (size_t)b * a.Lk + s, 1);
+  a.ws_list[p] = (int)(row * kpad + slot);
+}
+
+// 1 KB of a chunk copied straight into LDS: lane i fills bytes 16i..16i+15
+// of the destination from base + off.  Waited for by the caller (vmcnt(0) and a
+// barrier).  `base` is wave-uniform.
+__device__ __forceinline__ void dma_1k(uint8_t* dst, const uint8_t* base, uint32_t off) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+               :: "v"(off), "s"(m0), "s"(base) : "memory", "m0");
+}
+
+// Partial products of one row: part[row*kpad + slot, :] (bf16) =
+//   (scale dZ)[slot, :] . Q  (+ P[slot, :] . dO on the value columns),
+// contracted over the 128 (padded) heads on bf16 MFMA in transposed form,
+// part^T = Q^T . (scale dZ)^T + dO^T . P^T: wave w holds Q^T and dO^T of the
+// 16-column tiles w, w + NW, ... (NW * TPW tiles cover the row exactly) as A
+// operands for the whole row, and the
+// key-major dZ / P chunks of 32 slots come through LDS as B operands shared by
+// all waves.  Each lane then holds 4 consecutive columns of one slot.
+// LDS rows (one slot, 128 heads = 256 bytes) store 16-byte piece lp at
+// physical piece lp ^ (slot & 15), so the 16 slots of a B fragment read hit 16
+// different bank groups.
+template <int DQK, int DV, int NW, int TPW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_part_kernel(AttnBwdArgs a) {
+  constexpr int NDT = DQK / 16;
+  constexpr int CH = kBChunk * kBHeads * 2;  // bytes of one chunk of dZ (or P)
+  static_assert(DQK % 16 == 0 && DV % 16 == 0 && NW * TPW == NDT, "column tiles must split evenly over the waves");
+  __shared__ __attribute__((aligned(16))) uint8_t buf[2][2][CH];  // [stage][dZ, P][slot][heads]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
-  const int nsl = (NDT + 3) / 4;
-  const int row = blockIdx.x / nsl;
-  const int t = 4 * (blockIdx.x % nsl) + wave;
-  if (t >= NDT) return;  // wave-uniform; no barrier follows
-  const int b = row / a.Lq;
+  const int row = blockIdx.x;
   const int nch = (a.k + kBChunk - 1) / kBChunk;
   const size_t kpad = (size_t)nch * kBChunk;
-  const int d = 16 * t + li;             // this lane's column (B operand and output)
-  const bool d_ok = d < DQK, v_ok = d < DV;
-  const bool any_v = 16 * t < DV;         // wave-uniform: the tile has value columns
 
-  // B operands [heads 32 hs + 8g .. +7] x [column d], held for the whole row
-  v8bf qb[4], gb[4];
+  // A operands: column 16t + li, heads 32 ks + 8g .. +7.  Absent heads, and
+  // dO on the rope columns, are zero (loads use clamped in-bounds addresses,
+  // then select), so every wave runs the same branch-free loop.
+  v8bf qa[TPW][4], ga[TPW][4];
 #pragma unroll
-  for (int hs = 0; hs < 4; ++hs) {
-    uint32_t qw[4], gw[4];
+  for (int j = 0; j < TPW; ++j) {
+    const int t = wave + NW * j;
+    const bool has_v = 16 * t < DV;  // wave-uniform
+    const int col = 16 * t + li;
+    const uint16_t* qrow = a.q + (size_t)row * a.H * DQK + col;
+    const float* grow = a.dout + (size_t)row * a.H * DV + (has_v ? col : 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float qv[2], gv[2];
+    for (int ks = 0; ks < 4; ++ks) {
+      // an opaque copy of the lane's first head keeps the compiler from
+      // holding every head's address across tiles (it recomputes them)
+      const int h0 = 32 * ks + 8 * (opaque_tid() >> 4 & 3);
+      uint32_t qw[4], gw[4];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int head = 32 * hs + 8 * g + 2 * e + u;
-        const bool ok = head < a.H;
-        qv[u] = ok && d_ok ? bf16_bits_to_float(a.q[((size_t)row * a.H + head) * DQK + d]) : 0.0f;
-        gv[u] = ok && v_ok ? a.dout[((size_t)row * a.H + head) * DV + d] : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        float qv[2], gv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int head = h0 + 2 * e + u;
+          const int hc = min(head, a.H - 1);
+          const bool ok = head < a.H;
+          const float x = bf16_bits_to_float(qrow[(size_t)hc * DQK]);
+          const float y = grow[(size_t)hc * DV];  // in bounds for rope tiles too
+          qv[u] = ok ? x : 0.0f;
+          gv[u] = ok && has_v ? y : 0.0f;
+        }
+        qw[e] = pack_bf16x2(qv[0], qv[1]);
+        gw[e] = pack_bf16x2(gv[0], gv[1]);
       }
-      qw[e] = pack_bf16x2(qv[0], qv[1]);
-      gw[e] = pack_bf16x2(gv[0], gv[1]);
+      // packed here: the empty asm keeps the compiler from sinking the
+      // conversion into the chunk loop (it would keep the unpacked values)
+      v4i qp = {(int)qw[0], (int)qw[1], (int)qw[2], (int)qw[3]};
+      v4i gp = {(int)gw[0], (int)gw[1], (int)gw[2], (int)gw[3]};
+      asm volatile("" : "+v"(qp), "+v"(gp));
+      qa[j][ks] = __builtin_bit_cast(v8bf, qp);
+      ga[j][ks] = __builtin_bit_cast(v8bf, gp);
     }
-    qb[hs] = __builtin_bit_cast(v8bf, (v4i){(int)qw[0], (int)qw[1], (int)qw[2], (int)qw[3]});
-    gb[hs] = __builtin_bit_cast(v8bf, (v4i){(int)gw[0], (int)gw[1], (int)gw[2], (int)gw[3]});
   }
 
-  const int32_t* idx_row = a.indices + (size_t)row * a.k;
-  float* dkv_seq = a.dkv + (size_t)b * a.Lk * DQK;
+  // chunk c of dZ and P (contiguous CH bytes each) -> buf[st]; 1 KB per copy
+  const uint8_t* zsrc = (const uint8_t*)(a.ws_dzk + (size_t)row * kpad * kBHeads);
+  const uint8_t* psrc = (const uint8_t*)(a.ws_pk + (size_t)row * kpad * kBHeads);
+  auto issue = [&](int c, int st) {
+    constexpr int BLOCKS = 2 * CH / 1024;
+#pragma unroll
+    for (int j = 0; j < (BLOCKS + NW - 1) / NW; ++j) {
+      const int blk = wave + NW * j;
+      if (blk < BLOCKS) {
+        const int arr = blk / (CH / 1024), sub = blk % (CH / 1024);
+        const int slot = 4 * sub + (lane >> 4);
+        const int lp = (lane & 15) ^ (slot & 15);
+        const uint8_t* base = (arr ? psrc : zsrc) + (size_t)c * CH;
+        dma_1k(&buf[st][arr][1024 * sub], base, (uint32_t)(slot * 256 + 16 * lp));
+      }
+    }
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   for (int c = 0; c < nch; ++c) {
+    const int st = c & 1;
+    if (c + 1 < nch) issue(c + 1, st ^ 1);
+    v4f acc[TPW][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      // A operands: key 32c + 16kt + li, heads 32 hs + 8g .. +7
-      const size_t abase = ((size_t)row * kpad + (size_t)c * kBChunk + 16 * kt + li) * kBHeads + 8 * g;
-      v4f accz = {0.0f, 0.0f, 0.0f, 0.0f}, accp = accz;
+    for (int j = 0; j < TPW; ++j) acc[j][0] = acc[j][1] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int hs = 0; hs < 4; ++hs) {
-        const v8bf za = __builtin_bit_cast(v8bf, *(const v4i*)(a.ws_dzk + abase + 32 * hs));
-        accz = mfma_bf16_16x16x32(za, qb[hs], accz);
-        if (any_v) {
-          const v8bf pa = __builtin_bit_cast(v8bf, *(const v4i*)(a.ws_pk + abase + 32 * hs));
-          accp = mfma_bf16_16x16x32(pa, gb[hs], accp);
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int slot = 16 * kt + li;
+        const int off = slot * 256 + 16 * ((4 * ks + g) ^ (slot & 15));
+        const v8bf zb = __builtin_bit_cast(v8bf, *(const v4i*)&buf[st][0][off]);
+        const v8bf pb = __builtin_bit_cast(v8bf, *(const v4i*)&buf[st][1][off]);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+          acc[j][kt] = mfma_bf16_16x16x32(qa[j][ks], zb, acc[j][kt]);
+          acc[j][kt] = mfma_bf16_16x16x32(ga[j][ks], pb, acc[j][kt]);
         }
       }
-      // lane: keys 16kt + 4g + r, column d
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lane: columns 16t + 4g .. +3 of slot 32c + 16kt + li
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int slot = c * kBChunk + 16 * kt + 4 * g + r;
-        const int s = slot < a.k ? idx_row[slot] : -1;
-        if (d_ok && s >= 0 && s < a.Lk)
-          unsafeAtomicAdd(dkv_seq + (size_t)s * DQK + d, a.scale * accz[r] + accp[r]);
+    for (int kt = 0; kt < 2; ++kt) {
+      uint16_t* prow = a.ws_part + ((size_t)row * kpad + (size_t)c * kBChunk + 16 * kt + li) * DQK;
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+        *(v2i*)(prow + 16 * (wave + NW * j) + 4 * g) = (v2i){(int)pack_bf16x2(acc[j][kt][0], acc[j][kt][1]),
+                                                             (int)pack_bf16x2(acc[j][kt][2], acc[j][kt][3])};
+    }
+    // the next chunk's copies are complete and every wave is done with this one
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+}
+
+// One wave per key (b, s): dkv[b, s, :] += sum of the partial rows its list
+// names, in fp32.  Lane l owns 16-byte pieces l, l + 64, ... of the row; the
+// list is read 64 entries at a time and each entry broadcast from its lane.
+template <int DQK>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_reduce_kernel(AttnBwdArgs a) {
+  constexpr int NP = DQK / 8;
+  constexpr int PPL = (NP + 63) / 64;
+  constexpr int U = 4;  // entries in flight
+  const int lane = threadIdx.x & 63;
+  const long long key = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (key >= (long long)a.B * a.Lk) return;
+  const int n = a.ws_cnt[key];
+  if (n == 0) return;
+  const int base = a.ws_off[key];
+  float acc[PPL][8];
+#pragma unroll
+  for (int pp = 0; pp < PPL; ++pp)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[pp][e] = 0.0f;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int m = min(64, n - i0);
+    const int mine = lane < m ? a.ws_list[base + i0 + lane] : 0;
+    for (int e = 0; e < m; e += U) {
+      v4i v[U][PPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pos = __builtin_amdgcn_readlane(mine, e + u);  // e + u < 64
+        const uint16_t* prow = a.ws_part + (size_t)pos * DQK;
+#pragma unroll
+        for (int pp = 0; pp < PPL; ++pp) {
+          const int piece = lane + 64 * pp;
+          v[u][pp] = e + u < m && piece < NP ? *(const v4i*)(prow + 8 * piece) : (v4i){0, 0, 0, 0};
+        }
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int pp = 0; pp < PPL; ++pp)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t x = (uint32_t)v[u][pp][w];
+            acc[pp][2 * w] += __uint_as_float(x << 16);
+            acc[pp][2 * w + 1] += __uint_as_float(x & 0xFFFF0000u);
+          }
+    }
+  }
+  float* drow = a.dkv + (size_t)key * DQK;
+#pragma unroll
+  for (int pp = 0; pp < PPL; ++pp) {
+    const int piece = lane + 64 * pp;
+    if (piece < NP) {
+      v4f* d = (v4f*)(drow + 8 * piece);
+      v4f lo = d[0], hi = d[1];
+      lo += (v4f){acc[pp][0], acc[pp][1], acc[pp][2], acc[pp][3]};
+      hi += (v4f){acc[pp][4], acc[pp][5], acc[pp][6], acc[pp][7]};
+      d[0] = lo;
+      d[1] = hi;
     }
   }
 }
 
-// Scores kernel: SPLIT blocks of NW1 waves per row; dq kernel: NW2 waves.
-template <int DQK, int DV, int NW1, int SPLIT, int NW2>
+// Workspace layout (byte offsets, each part 256-byte aligned).
+struct BwdLayout {
+  size_t dzf, pk, dzk, part, list, cnt, off, cur, bsum, total;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(int B, int Lq, int Lk, int k, int dqk) {
+  const size_t rows = (size_t)B * Lq;
+  const size_t kpad = (size_t)(k + kBChunk - 1) / kBChunk * kBChunk;
+  const size_t keys = (size_t)B * Lk;
+  const size_t hm = align256(rows * kpad * kBHeads * sizeof(uint16_t));
+  BwdLayout l{};
+  l.dzf = 0;
+  l.pk = l.dzf + hm;
+  l.dzk = l.pk + hm;
+  l.part = l.dzk + hm;
+  l.list = l.part + align256(rows * kpad * dqk * sizeof(uint16_t));
+  l.cnt = l.list + align256(rows * k * sizeof(int32_t));
+  l.off = l.cnt + align256(keys * sizeof(int32_t));
+  l.cur = l.off + align256(keys * sizeof(int32_t));
+  l.bsum = l.cur + align256(keys * sizeof(int32_t));
+  l.total = l.bsum + align256((keys + kScanBlock - 1) / kScanBlock * sizeof(int32_t));
+  return l;
+}
+
+// Scores kernel: SPLIT blocks of NW1 waves per row; dq kernel: NW2 waves;
+// partial-product kernel: NW3 waves with TPW column tiles each.
+template <int DQK, int DV, int NW1, int SPLIT, int NW2, int NW3, int TPW>
 hipError_t launch_bwd_shape(const AttnBwdArgs& a, hipStream_t stream) {
   using S1 = BwdShape<DQK, DV, NW1 * SPLIT>;
   using S2 = BwdShape<DQK, DV, NW2>;
@@ -482,26 +753,61 @@ hipError_t launch_bwd_shape(const AttnBwdArgs& a, hipStream_t stream) {
   if (attr1 != hipSuccess) return attr1;
   if (attr2 != hipSuccess) return attr2;
   const unsigned rows = (unsigned)((long long)a.B * a.Lq);
-  hipError_t e = launch_kernel((const void*)attn_bwd_scores_kernel<DQK, DV, NW1, SPLIT>, dim3(rows * SPLIT),
-                               dim3(64 * NW1), smem1, stream, a);
+  const long long entries = (long long)rows * a.k;
+  const long long keys = (long long)a.B * a.Lk;
+  const unsigned nb = (unsigned)((keys + kScanBlock - 1) / kScanBlock);
+  const unsigned eb = (unsigned)((entries + 255) / 256);
+
+  // key lists of the (row, slot) pairs
+  hipError_t e = launch_kernel((const void*)bwd_zero_kernel, dim3((unsigned)std::min<long long>((keys + 255) / 256, 4096)),
+                               dim3(256), 0, stream, a.ws_cnt, keys);
   if (e != hipSuccess) return e;
-  e = launch_kernel((const void*)attn_bwd_dq_kernel<DQK, DV, NW2>, dim3(rows), dim3(64 * NW2), smem2, stream, a);
-  if (e != hipSuccess) return e;
-  const unsigned nsl = (unsigned)((S2::NDT + 3) / 4);
-  return launch_kernel((const void*)attn_bwd_dkv_kernel<DQK, DV>, dim3(rows * nsl), dim3(256), 0, stream, a);
+  if ((e = launch_kernel((const void*)bwd_count_kernel, dim3(eb), dim3(256), 0, stream, a)) != hipSuccess) return e;
+  if ((e = launch_kernel((const void*)bwd_scan_sums_kernel, dim3(nb), dim3(kScanThreads), 0, stream,
+                         (const int32_t*)a.ws_cnt, a.ws_bsum, keys)) != hipSuccess)
+    return e;
+  if ((e = launch_kernel((const void*)bwd_scan_top_kernel, dim3(1), dim3(1024), 0, stream, a.ws_bsum, (int)nb)) !=
+      hipSuccess)
+    return e;
+  if ((e = launch_kernel((const void*)bwd_scan_apply_kernel, dim3(nb), dim3(kScanThreads), 0, stream, a, keys)) !=
+      hipSuccess)
+    return e;
+  if ((e = launch_kernel((const void*)bwd_fill_kernel, dim3(eb), dim3(256), 0, stream, a)) != hipSuccess) return e;
+
+  if ((e = launch_kernel((const void*)attn_bwd_scores_kernel<DQK, DV, NW1, SPLIT>, dim3(rows * SPLIT), dim3(64 * NW1),
+                         smem1, stream, a)) != hipSuccess)
+    return e;
+  if ((e = launch_kernel((const void*)attn_bwd_dq_kernel<DQK, DV, NW2>, dim3(rows), dim3(64 * NW2), smem2, stream,
+                         a)) != hipSuccess)
+    return e;
+  if ((e = launch_kernel((const void*)attn_bwd_dkv_part_kernel<DQK, DV, NW3, TPW>, dim3(rows), dim3(64 * NW3), 0,
+                         stream, a)) != hipSuccess)
+    return e;
+  return launch_kernel((const void*)attn_bwd_dkv_reduce_kernel<DQK>, dim3((unsigned)((keys + 3) / 4)), dim3(256), 0,
+                       stream, a);
 }
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int rows, int k) {
-  const size_t kpad = (size_t)(k + kBChunk - 1) / kBChunk * kBChunk;
-  // dZ in operand order + P and dZ key-major, bf16, 128 padded heads each
-  return 3 * (size_t)rows * kpad * kBHeads * sizeof(uint16_t);
+size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int k, int dqk) {
+  return bwd_layout(B, Lq, Lk, k, dqk).total;
 }
 
-hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& a, hipStream_t stream) {
-  if (a.Dv == 512 && a.Dr == 64) return launch_bwd_shape<576, 512, 4, 2, 8>(a, stream);
-  if (a.Dv == 64 && a.Dr == 16) return launch_bwd_shape<80, 64, 4, 1, 4>(a, stream);
+hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& args, void* workspace, hipStream_t stream) {
+  AttnBwdArgs a = args;
+  const BwdLayout l = bwd_layout(a.B, a.Lq, a.Lk, a.k, a.Dv + a.Dr);
+  uint8_t* w = (uint8_t*)workspace;
+  a.ws_dzf = (uint16_t*)(w + l.dzf);
+  a.ws_pk = (uint16_t*)(w + l.pk);
+  a.ws_dzk = (uint16_t*)(w + l.dzk);
+  a.ws_part = (uint16_t*)(w + l.part);
+  a.ws_list = (int32_t*)(w + l.list);
+  a.ws_cnt = (int32_t*)(w + l.cnt);
+  a.ws_off = (int32_t*)(w + l.off);
+  a.ws_cur = (int32_t*)(w + l.cur);
+  a.ws_bsum = (int32_t*)(w + l.bsum);
+  if (a.Dv == 512 && a.Dr == 64) return launch_bwd_shape<576, 512, 4, 2, 8, 12, 3>(a, stream);
+  if (a.Dv == 64 && a.Dr == 16) return launch_bwd_shape<80, 64, 4, 1, 4, 5, 1>(a, stream);
   return hipErrorInvalidValue;
 }
 

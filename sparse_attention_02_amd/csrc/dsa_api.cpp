@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -77,6 +78,21 @@ int check_attn(const dsa_problem* p) {
                 "kv_len %d: the latent gather needs kv_len <= 2^24 and one sequence's cache "
                 "below 4 GiB - 8 KiB", p->kv_len);
   return DSA_OK;
+}
+
+// The backward's key lists name a (row, slot) pair as row * kpad + slot and
+// count entries per key in 32-bit integers.
+int check_bwd_size(const dsa_problem* p) {
+  const long long kpad = (p->topk + 31) / 32 * 32;
+  if ((long long)p->batch * p->q_len * kpad > INT32_MAX || (long long)p->batch * p->kv_len > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "sparse_mla_attn_bwd: batch*q_len*topk (topk rounded up to 32) and batch*kv_len must "
+                "stay below 2^31");
+  return DSA_OK;
+}
+
+size_t bwd_ws_bytes(const dsa_problem* p) {
+  return dsa::attn_bwd_workspace_bytes(p->batch, p->q_len, p->kv_len, p->topk, p->d_latent + p->d_rope);
 }
 
 int check_ptr(const void* ptr, const char* name, size_t align) {
@@ -167,7 +183,7 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
     case DSA_OP_SPARSE_MLA_ATTN:
       return check_attn(p) ? bad : attn_ws_bytes(p);
     case DSA_OP_SPARSE_MLA_ATTN_BWD:
-      return check_attn(p) ? bad : dsa::attn_bwd_workspace_bytes(p->batch * p->q_len, p->topk);
+      return check_attn(p) || check_bwd_size(p) ? bad : bwd_ws_bytes(p);
     case DSA_OP_FORWARD:
       if (check_index(p) || check_attn(p)) return bad;
       return round_up(scores_bytes(p)) + round_up(indices_bytes(p)) +
@@ -239,24 +255,21 @@ int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint1
   if (int s = check_ptr(dout, "dout", 16)) return s;
   if (int s = check_ptr(dq, "dq", 16)) return s;
   if (int s = check_ptr(dkv, "dkv", 16)) return s;
-  const long long rows = (long long)p->batch * p->q_len;
-  const size_t need = dsa::attn_bwd_workspace_bytes((int)rows, p->topk);
+  if (int s = check_bwd_size(p)) return s;
+  const size_t need = bwd_ws_bytes(p);
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "sparse_mla_attn_bwd needs %zu workspace bytes, got %zu", need,
                 workspace_bytes);
-  if (!aligned(workspace, 16)) return fail(DSA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (!aligned(workspace, 256)) return fail(DSA_ERR_ALIGN, "workspace is not 256-byte aligned");
   dsa::AttnBwdArgs a{};
   a.q = q; a.kv = kv; a.indices = indices; a.out = out; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dkv = dkv;
-  const size_t part = need / 3 / sizeof(uint16_t);  // [rows, kpad, 128] bf16 each
-  a.ws_dzf = (uint16_t*)workspace;
-  a.ws_pk = a.ws_dzf + part;
-  a.ws_dzk = a.ws_pk + part;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.H = p->heads;
   a.Dv = p->d_latent; a.Dr = p->d_rope; a.k = p->topk;
   a.scale = p->softmax_scale;
   a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
-  return hip_status(dsa::launch_sparse_mla_attn_bwd(a, (hipStream_t)stream), "sparse_mla_attn_bwd launch");
+  return hip_status(dsa::launch_sparse_mla_attn_bwd(a, workspace, (hipStream_t)stream),
+                    "sparse_mla_attn_bwd launch");
 }
 
 int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,

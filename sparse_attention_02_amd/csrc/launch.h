@@ -55,22 +55,32 @@ struct AttnBwdArgs {
   const float* dout;        // [B, Lq, H, Dv]  upstream gradient
   float* dq;                // [B, Lq, H, Dqk] written
   float* dkv;               // [B, Lk, Dqk]    accumulated into
-  // workspace: dZ in operand order, P and dZ key-major ([B*Lq, kpad, 128] bf16)
+  // workspace parts, set by launch_sparse_mla_attn_bwd from one buffer:
+  // dZ in operand order, P and scale * dZ key-major ([B*Lq, kpad, 128] bf16),
+  // partial dkv rows per (row, slot) ([B*Lq, kpad, Dqk] bf16), the (row, slot)
+  // lists of every key with their counts and offsets, scan block sums
   uint16_t* ws_dzf;
   uint16_t* ws_pk;
   uint16_t* ws_dzk;
+  uint16_t* ws_part;
+  int32_t* ws_list;
+  int32_t* ws_cnt;
+  int32_t* ws_off;
+  int32_t* ws_cur;
+  int32_t* ws_bsum;
   int B, Lq, Lk, H, Dv, Dr, k;
   float scale;              // softmax_scale
   float scale_log2;         // softmax_scale * log2(e)
 };
 
-// Launch `kernel(arg)` and return the launch's own status (not the thread's
-// sticky last-error state, which other libraries in the process also write).
-template <typename Arg>
+// Launch `kernel(args...)` and return the launch's own status (not the
+// thread's sticky last-error state, which other libraries in the process also
+// write).  The argument types must match the kernel's parameters exactly.
+template <typename... Args>
 inline hipError_t launch_kernel(const void* kernel, dim3 grid, dim3 block, size_t smem,
-                                hipStream_t stream, const Arg& arg) {
-  void* args[] = {const_cast<Arg*>(&arg)};
-  return hipLaunchKernel(kernel, grid, block, args, smem, stream);
+                                hipStream_t stream, const Args&... args) {
+  void* ptrs[] = {const_cast<Args*>(&args)...};
+  return hipLaunchKernel(kernel, grid, block, ptrs, smem, stream);
 }
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
@@ -83,8 +93,10 @@ hipError_t launch_masked_mha_attn(const AttnArgs& a, hipStream_t stream);
 // Parts per row when few rows would leave most CUs idle (1: no split), and the
 // workspace the split needs.
 int attn_splits(int rows, int k);
-hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& a, hipStream_t stream);
-size_t attn_bwd_workspace_bytes(int rows, int k);
+// `workspace` holds attn_bwd_workspace_bytes(B, Lq, Lk, k, Dv + Dr) bytes,
+// 256-byte aligned; the ws_* members of `a` are ignored and set from it.
+hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t stream);
+size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int k, int dqk);
 size_t attn_workspace_bytes(int rows, int k, int H, int Dv);
 
 }  // namespace dsa

@@ -109,20 +109,32 @@ def test_masked_mode_checks():
     assert s == -3
 
 
+def _bwd_ws(B, Lq, Lk, k, dqk):
+    # the sizes dsa.h documents for the backward's workspace
+    r, kp = B * Lq, -(-k // 32) * 32
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    return (3 * up(r * kp * 128 * 2) + up(r * kp * dqk * 2) + up(r * k * 4) + 3 * up(B * Lk * 4)
+            + up(-(-(B * Lk) // 4096) * 4))
+
+
 def test_backward_checks():
-    # P and dZ of every (row, selected entry, head) in bf16, three copies
-    # (operand order for dq, key-major for dkv), entries padded to 32, heads to 128
-    assert dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == 3 * 256 * 64 * 128 * 2
-    assert dsa.workspace_size(MLA, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == 3 * 4096 * 2048 * 128 * 2
+    assert dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == _bwd_ws(1, 256, 256, 64, 80)
+    assert dsa.workspace_size(MLA, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == _bwd_ws(1, 4096, 4096, 2048, 576)
     odd = Problem(**{**GOOD.__dict__, "topk": 65})
-    assert dsa.workspace_size(odd, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == 3 * 256 * 96 * 128 * 2
+    assert dsa.workspace_size(odd, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == _bwd_ws(1, 256, 256, 65, 80)
+    # padded entries: 3 * rows * 96 * 128 bf16 of P / dZ for k = 65
+    assert _bwd_ws(1, 256, 256, 65, 80) > 3 * 256 * 96 * 128 * 2
+    # the lists index (row, entry) pairs in 32 bits
+    huge = Problem(8, 131072, 131072, 0, 64, 128, 2048, 128, 512, 64)
+    with pytest.raises(DsaError):
+        dsa.workspace_size(huge, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD)
     need = dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD)
     args = [FAKE] * 8
     s, msg = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, FAKE, need - 1, stream=0)
     assert s == -4 and str(need) in msg
     s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, None, need, stream=0)
     assert s == -4
-    s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, FAKE + 8, need, stream=0)
+    s, _ = _status(dsa.dsa_sparse_mla_attn_bwd, GOOD, *args, FAKE + 128, need, stream=0)
     assert s == -5
     for i, name in enumerate(["q", "kv", "indices", "out", "lse", "dout", "dq", "dkv"]):
         a = list(args)
