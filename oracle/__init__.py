@@ -62,6 +62,12 @@ def lib():
         L.dsa_oracle_sparse_mla_attn_bwd.argtypes = [i32, i32, i32, i32, i32, f32, i64,
                                                      vp, vp, vp, vp, vp, vp, vp]
         L.dsa_oracle_sparse_mla_attn_bwd.restype = None
+        L.dsa_oracle_warmup_target.argtypes = [i32, i32, i32, f32, i64, vp, vp, vp, vp, vp]
+        L.dsa_oracle_warmup_target.restype = None
+        L.dsa_oracle_warmup_kl.argtypes = [i32, i64, vp, vp, vp, vp, vp]
+        L.dsa_oracle_warmup_kl.restype = None
+        L.dsa_oracle_index_scores_bwd.argtypes = [i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.dsa_oracle_index_scores_bwd.restype = None
         L.dsa_oracle_max_threads.argtypes = []
         L.dsa_oracle_max_threads.restype = ctypes.c_int
         _lib = L
@@ -181,6 +187,71 @@ def sparse_mla_attn_bwd(kv, q_rows, indices, row_batch, dout_rows, d_latent: int
                                          rbp, qp, kv.ctypes.data, ip, gp, dq.ctypes.data,
                                          dkv.ctypes.data)
     return dq, dkv
+
+
+def warmup_target(kv, q_rows, row_batch, row_pos, softmax_scale: float, fill=np.nan) -> np.ndarray:
+    """The dense warm-up's target distribution in double precision (DeepSeek-V3.2
+    spec sheet, design overview: the main attention distribution summed over
+    the heads): target[r, s] = mean over heads of the softmax over
+    s' <= pos_r of softmax_scale * q . kv[s'], for s <= pos_r; `fill` after.
+    kv [B, Lk, Dqk] bf16 bits, q_rows [R, H, Dqk] bf16 bits."""
+    kv = np.ascontiguousarray(kv, dtype=np.uint16)
+    B, Lk, Dqk = kv.shape
+    q_rows, qp = _c(q_rows, np.uint16)
+    R, H, Dqk2 = q_rows.shape
+    assert Dqk2 == Dqk
+    rb, rbp = _c(row_batch, np.int32)
+    rpos, rpp = _c(row_pos, np.int32)
+    assert rb.shape == (R,) and rpos.shape == (R,) and (rb >= 0).all() and (rb < B).all()
+    assert (rpos >= 0).all()
+    out = np.full((R, Lk), fill, dtype=np.float64)
+    lib().dsa_oracle_warmup_target(Lk, H, Dqk, float(softmax_scale), R, rbp, rpp, qp, kv.ctypes.data,
+                                   out.ctypes.data)
+    return out
+
+
+def warmup_kl(scores_rows, target_rows, row_pos, fill=np.nan):
+    """KL(target || softmax(scores)) per row over s <= pos_r and its gradient
+    with respect to the scores, softmax(scores) - target, in double precision
+    (the dense warm-up's indexer objective).  scores_rows, target_rows [R, Lk]
+    float32 (entries past pos_r are not read).  Returns (loss [R], dscores
+    [R, Lk] with `fill` past pos_r)."""
+    I, Ip = _c(scores_rows, np.float32)
+    P, Pp = _c(target_rows, np.float32)
+    R, Lk = I.shape
+    assert P.shape == (R, Lk)
+    rpos, rpp = _c(row_pos, np.int32)
+    assert rpos.shape == (R,) and (rpos >= 0).all()
+    loss = np.empty(R, dtype=np.float64)
+    d = np.full((R, Lk), fill, dtype=np.float64)
+    lib().dsa_oracle_warmup_kl(Lk, R, rpp, Ip, Pp, loss.ctypes.data, d.ctypes.data)
+    return loss, d
+
+
+def index_scores_bwd(k_idx, q_idx_rows, w_rows, row_batch, row_pos, dscores_rows):
+    """Gradients of the indexer scores with respect to q_I, w and k_I for a
+    gradient dscores_rows [R, Lk] of the scores (entries past pos_r unused), in
+    double precision; the ReLU's derivative is taken as 0 at 0.  Returns
+    (dq_idx [R, H_I, d_I], dw [R, H_I], dk_idx [B, Lk, d_I]); dk_idx sums the
+    given rows only."""
+    k_idx = np.ascontiguousarray(k_idx, dtype=np.uint8)
+    B, Lk, dI = k_idx.shape
+    q, qp = _c(q_idx_rows, np.uint8)
+    R, HI, dI2 = q.shape
+    assert dI2 == dI
+    w, wp = _c(w_rows, np.float32)
+    assert w.shape == (R, HI)
+    rb, rbp = _c(row_batch, np.int32)
+    rpos, rpp = _c(row_pos, np.int32)
+    assert rb.shape == (R,) and rpos.shape == (R,) and (rb >= 0).all() and (rb < B).all()
+    g, gp = _c(dscores_rows, np.float64)
+    assert g.shape == (R, Lk)
+    dq = np.empty((R, HI, dI), dtype=np.float64)
+    dw = np.empty((R, HI), dtype=np.float64)
+    dk = np.zeros((B, Lk, dI), dtype=np.float64)
+    lib().dsa_oracle_index_scores_bwd(Lk, HI, dI, R, rbp, rpp, qp, wp, k_idx.ctypes.data, gp,
+                                      dq.ctypes.data, dw.ctypes.data, dk.ctypes.data)
+    return dq, dw, dk
 
 
 def masked_mha_attn(kv, q_rows, indices, row_batch, row_pos, d_latent: int, softmax_scale: float):

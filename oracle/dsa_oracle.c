@@ -45,6 +45,19 @@
  *    row gets dkv[s_i] += scale * dz_i q, plus p_i dout on its value columns.
  *    Each index entry is one term, as in the forward.  The gradient does not
  *    flow into the selection (the indices are fixed).
+ *  - Dense warm-up objective (DeepSeek-V3.2 spec sheet, design overview and
+ *    the curriculum row of its training table; "DeepSeek V3.2 and the
+ *    lightning indexer", training section): only the indexer is trained, so
+ *    that its softmax over the scores of a query matches the main attention's
+ *    distribution summed over the heads, under a KL loss.  Readings: the main
+ *    attention here is dense over s <= pos(t) (the warm-up keeps it dense);
+ *    the summed distribution is divided by the head count so that it is a
+ *    distribution, p[t,s] = (1/H) sum_h softmax_s(z[t,h,s]); the loss of a
+ *    row is KL(p_t || softmax(I_t)) with the target first, and its gradient
+ *    with respect to the scores is softmax(I_t) - p_t.  Back through the
+ *    indexer, with u = q_I[t,j] . k_I[s] and the ReLU's derivative taken as 0
+ *    at u = 0: dw[t,j] = sum_s dI[t,s] ReLU(u), dq_I[t,j] = w[t,j] sum_s
+ *    dI[t,s] [u > 0] k_I[s], dk_I[s] = sum_(t,j) dI[t,s] w[t,j] [u > 0] q_I[t,j].
  *
  * Query rows are given explicitly (batch index, absolute position and the
  * row's own query data), so any subset of a workload's rows can be evaluated.
@@ -342,6 +355,125 @@ void dsa_oracle_sparse_mla_attn_bwd(int32_t kv_len, int32_t heads, int32_t d_lat
       }
     }
   free(pz);
+}
+
+/* ---------------------------------------------------------------------------
+ * Dense warm-up objective
+ * ------------------------------------------------------------------------- */
+
+/* target[r, s] = (1/heads) sum_h softmax over s' <= pos_r of
+ * softmax_scale * q_rows[r,h,:] . kv[b_r, s', :], for s in [0, min(pos_r, Lk-1)];
+ * other entries are untouched.  Double precision throughout. */
+void dsa_oracle_warmup_target(int32_t kv_len, int32_t heads, int32_t dqk, float softmax_scale,
+                              int64_t nrows, const int32_t* row_batch, const int32_t* row_pos,
+                              const uint16_t* q_rows, const uint16_t* kv, double* target) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const uint16_t* cache = kv + (int64_t)row_batch[r] * kv_len * dqk;
+    const int32_t n = row_pos[r] + 1 < kv_len ? row_pos[r] + 1 : kv_len;
+    double* z = (double*)malloc((size_t)n * sizeof(double));
+    double* qh = (double*)malloc((size_t)dqk * sizeof(double));
+    double* t = target + r * kv_len;
+    for (int32_t s = 0; s < n; ++s) t[s] = 0.0;
+    for (int32_t h = 0; h < heads; ++h) {
+      for (int d = 0; d < dqk; ++d) qh[d] = bf16_to_double(q_rows[(r * heads + h) * dqk + d]);
+      double zmax = -INFINITY;
+      for (int32_t s = 0; s < n; ++s) {
+        const uint16_t* row = cache + (int64_t)s * dqk;
+        double dot = 0.0;
+        for (int d = 0; d < dqk; ++d) dot += qh[d] * bf16_to_double(row[d]);
+        z[s] = (double)softmax_scale * dot;
+        if (z[s] > zmax) zmax = z[s];
+      }
+      double Z = 0.0;
+      for (int32_t s = 0; s < n; ++s) Z += exp(z[s] - zmax);
+      for (int32_t s = 0; s < n; ++s) t[s] += exp(z[s] - zmax) / Z / heads;
+    }
+    free(z);
+    free(qh);
+  }
+}
+
+/* Per row r over s in [0, min(pos_r, Lk-1)]: with the indexer distribution
+ * pi = softmax(scores[r, .]), loss[r] = sum_s target (log target - log pi)
+ * (terms with target = 0 are 0) and dscores[r, s] = pi_s - target_s, the
+ * gradient of the summed loss.  Other dscores entries are untouched. */
+void dsa_oracle_warmup_kl(int32_t kv_len, int64_t nrows, const int32_t* row_pos, const float* scores,
+                          const float* target, double* loss, double* dscores) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int32_t n = row_pos[r] + 1 < kv_len ? row_pos[r] + 1 : kv_len;
+    const float* I = scores + r * kv_len;
+    const float* p = target + r * kv_len;
+    double m = -INFINITY;
+    for (int32_t s = 0; s < n; ++s) m = (double)I[s] > m ? (double)I[s] : m;
+    double Z = 0.0;
+    for (int32_t s = 0; s < n; ++s) Z += exp((double)I[s] - m);
+    const double logZ = m + log(Z);
+    double l = 0.0;
+    for (int32_t s = 0; s < n; ++s) {
+      const double log_pi = (double)I[s] - logZ;
+      const double ps = (double)p[s];
+      if (ps > 0.0) l += ps * (log(ps) - log_pi);
+      dscores[r * kv_len + s] = exp(log_pi) - ps;
+    }
+    loss[r] = l;
+  }
+}
+
+/* Gradients of the indexer scores with respect to its inputs, for the given
+ * rows and a gradient dscores [nrows, kv_len] of the scores (entries past
+ * pos_r are not read): dq_idx [nrows, H_I, d_I] and dw [nrows, H_I] written,
+ * dk_idx [B, kv_len, d_I] accumulated into.  The ReLU's derivative is 0 at 0. */
+void dsa_oracle_index_scores_bwd(int32_t kv_len, int32_t idx_heads, int32_t idx_dim, int64_t nrows,
+                                 const int32_t* row_batch, const int32_t* row_pos,
+                                 const uint8_t* q_idx_rows, const float* w_rows, const uint8_t* k_idx,
+                                 const double* dscores, double* dq_idx, double* dw, double* dk_idx) {
+  double lut[256];
+  for (int c = 0; c < 256; ++c) lut[c] = dsa_oracle_e4m3_to_double((uint8_t)c);
+  /* per row in parallel; the key gradient is summed serially afterwards */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const uint8_t* keys = k_idx + (int64_t)row_batch[r] * kv_len * idx_dim;
+    const int32_t n = row_pos[r] + 1 < kv_len ? row_pos[r] + 1 : kv_len;
+    for (int32_t j = 0; j < idx_heads; ++j) {
+      const uint8_t* q = q_idx_rows + (r * idx_heads + j) * idx_dim;
+      const double wj = (double)w_rows[r * idx_heads + j];
+      double* dq = dq_idx + (r * idx_heads + j) * idx_dim;
+      double dwj = 0.0;
+      for (int d = 0; d < idx_dim; ++d) dq[d] = 0.0;
+      for (int32_t s = 0; s < n; ++s) {
+        const uint8_t* k = keys + (int64_t)s * idx_dim;
+        double u = 0.0;
+        for (int d = 0; d < idx_dim; ++d) u += lut[q[d]] * lut[k[d]];
+        if (u > 0.0) {
+          const double g = dscores[r * kv_len + s];
+          dwj += g * u;
+          for (int d = 0; d < idx_dim; ++d) dq[d] += g * wj * lut[k[d]];
+        }
+      }
+      dw[r * idx_heads + j] = dwj;
+    }
+  }
+  for (int64_t r = 0; r < nrows; ++r) {
+    const uint8_t* keys = k_idx + (int64_t)row_batch[r] * kv_len * idx_dim;
+    double* dk_seq = dk_idx + (int64_t)row_batch[r] * kv_len * idx_dim;
+    const int32_t n = row_pos[r] + 1 < kv_len ? row_pos[r] + 1 : kv_len;
+#pragma omp parallel for schedule(static)
+    for (int32_t s = 0; s < n; ++s) {
+      const uint8_t* k = keys + (int64_t)s * idx_dim;
+      const double g = dscores[r * kv_len + s];
+      for (int32_t j = 0; j < idx_heads; ++j) {
+        const uint8_t* q = q_idx_rows + (r * idx_heads + j) * idx_dim;
+        double u = 0.0;
+        for (int d = 0; d < idx_dim; ++d) u += lut[q[d]] * lut[k[d]];
+        if (u > 0.0) {
+          const double c = g * (double)w_rows[r * idx_heads + j];
+          for (int d = 0; d < idx_dim; ++d) dk_seq[(int64_t)s * idx_dim + d] += c * lut[q[d]];
+        }
+      }
+    }
+  }
 }
 
 int dsa_oracle_max_threads(void) {

@@ -9,8 +9,8 @@ the weighted head sum; the causal and top-k pins fix the candidate set and the
 order; dense equivalence fixes attention when nothing is dropped.
 
 Sources: "DeepSeek V3.2 and the lightning indexer" (section "How the lightning
-indexer works") and the DeepSeek-V3.2 spec sheet (design overview, section
-2.1).
+indexer works", training section) and the DeepSeek-V3.2 spec sheet (design
+overview, section 2.1, the training table's curriculum row).
 """
 import math
 
@@ -486,6 +486,126 @@ def test_attention_backward_closed_forms():
     idx = np.stack([rng.choice(L, size=k, replace=False) for _ in range(2)]).astype(np.int32)
     _, dkv = oracle.sparse_mla_attn_bwd(kv_, q_, idx, np.zeros(2, np.int32), g, Dv, 0.5, 1)
     np.testing.assert_allclose(dkv[0, :, Dv:].sum(0), 0.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Dense warm-up objective
+# ---------------------------------------------------------------------------
+
+def test_warmup_target_is_head_mean_of_sdpa_weights():
+    """With one-hot value columns the attention output of each head is its
+    probability vector, so torch's SDPA (fp64, causal) gives the target as the
+    mean of its outputs over the heads."""
+    rng = RNG(20)
+    L, H, Dr = 12, 3, 4
+    onehot = np.eye(L)
+    kvv = np.concatenate([onehot, rng.normal(size=(L, Dr))], axis=1)
+    kv_ = bf16_bits(kvv)[None]
+    q_ = bf16_bits(rng.normal(size=(L, H, L + Dr)))
+    scale = 0.75  # exact in fp32, the type the oracle takes it in
+    t = oracle.warmup_target(kv_, q_, np.zeros(L, np.int32), np.arange(L, dtype=np.int32), scale, fill=0.0)
+    Q = torch.from_numpy(bf16_vals(q_)).permute(1, 0, 2)
+    K = torch.from_numpy(bf16_vals(kv_[0])).expand(H, L, L + Dr)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, K[..., :L], is_causal=True, scale=scale)
+    np.testing.assert_allclose(t, o.mean(0).numpy(), atol=1e-14, rtol=0)
+
+
+def test_warmup_target_special_cases():
+    rng = RNG(21)
+    L, H, D = 9, 4, 8
+    kv_ = bf16_bits(rng.normal(size=(1, L, D)))
+    rb, pos = np.zeros(L, np.int32), np.arange(L, dtype=np.int32)
+    # zero queries: uniform over the causal range
+    t = oracle.warmup_target(kv_, np.zeros((L, H, D), np.uint16), rb, pos, 0.5, fill=0.0)
+    for r in range(L):
+        np.testing.assert_allclose(t[r, : r + 1], 1.0 / (r + 1), rtol=1e-15)
+        assert (t[r, r + 1:] == 0).all()
+    # identical heads: one head's softmax (torch, fp64)
+    q1 = bf16_bits(rng.normal(size=(L, 1, D)))
+    tq = oracle.warmup_target(kv_, np.repeat(q1, H, axis=1), rb, pos, 0.5, fill=0.0)
+    z = 0.5 * bf16_vals(q1[:, 0]) @ bf16_vals(kv_[0]).T
+    z = torch.from_numpy(z).masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), -math.inf)
+    np.testing.assert_allclose(tq, torch.softmax(z, -1).numpy(), atol=1e-15)
+    # rows sum to one; head order does not matter
+    q_ = bf16_bits(rng.normal(size=(L, H, D)))
+    t = oracle.warmup_target(kv_, q_, rb, pos, 0.5, fill=0.0)
+    np.testing.assert_allclose(t.sum(1), 1.0, rtol=1e-14)
+    tp = oracle.warmup_target(kv_, q_[:, ::-1], rb, pos, 0.5, fill=0.0)
+    np.testing.assert_allclose(tp, t, rtol=1e-14, atol=1e-300)
+
+
+def test_warmup_kl_matches_scipy_entropy_and_gradient():
+    from scipy.special import rel_entr  # p log(p / q) termwise, 0 where p = 0, no renormalising
+    rng = RNG(22)
+    R, Lk = 5, 16
+    pos = np.array([0, 3, 7, 15, 10], np.int32)
+    I = rng.normal(size=(R, Lk)).astype(np.float32) * 3
+    P = rng.random(size=(R, Lk)).astype(np.float32)
+    P[1, 2] = 0.0  # a zero target entry contributes nothing
+    for r in range(R):
+        P[r, pos[r] + 1:] = 0
+        P[r] /= P[r].sum()
+    loss, d = oracle.warmup_kl(I, P, pos)
+    for r in range(R):
+        n = pos[r] + 1
+        pi = torch.softmax(torch.from_numpy(I[r, :n].astype(np.float64)), 0).numpy()
+        assert loss[r] == pytest.approx(rel_entr(P[r, :n].astype(np.float64), pi).sum(), rel=1e-12, abs=1e-15)
+        np.testing.assert_allclose(d[r, :n], pi - P[r, :n], atol=1e-15)
+        assert np.isnan(d[r, n:]).all()
+        # softmax sums to one, so the gradient sums to 1 - sum(P) (P is fp32)
+        assert d[r, :n].sum() == pytest.approx(1.0 - P[r, :n].astype(np.float64).sum(), abs=1e-14)
+    assert loss[0] == 0.0 and (loss >= 0).all()
+    # the gradient is the derivative of the loss (central differences)
+    r, h = 3, 1e-3
+    for s in range(pos[r] + 1):
+        Ip, Im = I.copy(), I.copy()
+        Ip[r, s] += h
+        Im[r, s] -= h
+        fd = (oracle.warmup_kl(Ip, P, pos)[0][r] - oracle.warmup_kl(Im, P, pos)[0][r]) / (float(Ip[r, s]) - float(Im[r, s]))
+        assert fd == pytest.approx(d[r, s], abs=2e-6)
+
+
+def test_warmup_kl_zero_at_match_and_shift_invariant():
+    rng = RNG(23)
+    R, Lk = 4, 12
+    pos = np.full(R, Lk - 1, np.int32)
+    I = rng.normal(size=(R, Lk)).astype(np.float32)
+    P = torch.softmax(torch.from_numpy(I.astype(np.float64)), -1).numpy().astype(np.float32)
+    loss, d = oracle.warmup_kl(I, P, pos)
+    assert np.abs(loss).max() < 1e-7 and np.abs(d).max() < 1e-7  # P rounded to fp32
+    P2 = rng.random(size=(R, Lk)).astype(np.float32)
+    P2 /= P2.sum(1, keepdims=True)
+    l1, d1 = oracle.warmup_kl(I, P2, pos)
+    l2, d2 = oracle.warmup_kl(I + np.float32(5.0), P2, pos)
+    np.testing.assert_allclose(l1, l2, rtol=1e-6)
+    np.testing.assert_allclose(d1, d2, atol=1e-6)
+
+
+def test_index_scores_bwd_matches_autograd():
+    """dq_I, dw and dk_I against torch autograd of the indexer formula on the
+    decoded values (fp64), with exact zeros of q.k on the grid (where the ReLU's
+    derivative is 0 in both)."""
+    rng = RNG(24)
+    R, Lk, HI, dI = 6, 20, 4, 16
+    qv = grid(rng, (R, HI, dI), -2, 2, 0.5)
+    qv[0, 0] = 0.0  # u = 0 for a whole head
+    kv_ = grid(rng, (2, Lk, dI), -2, 2, 0.5)
+    w = grid(rng, (R, HI), -1, 1, 0.25).astype(np.float32)
+    rb = np.array([0, 0, 1, 1, 0, 1], np.int32)
+    pos = np.array([0, 5, 19, 11, 19, 3], np.int32)
+    g = rng.normal(size=(R, Lk))
+    dq, dw, dk = oracle.index_scores_bwd(enc_e4m3(kv_), enc_e4m3(qv), w, rb, pos, g)
+    Q = torch.tensor(qv, dtype=torch.float64, requires_grad=True)
+    K = torch.tensor(kv_, dtype=torch.float64, requires_grad=True)
+    W = torch.tensor(w, dtype=torch.float64, requires_grad=True)
+    u = torch.einsum("rjd,rsd->rjs", Q, K[torch.from_numpy(rb).long()])
+    I = (W[..., None] * torch.relu(u)).sum(1)
+    mask = torch.arange(Lk)[None, :] <= torch.from_numpy(pos)[:, None]
+    (I * torch.from_numpy(g) * mask).sum().backward()
+    np.testing.assert_allclose(dq, Q.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dw, W.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, K.grad.numpy(), atol=1e-12)
+    assert (dq[0, 0] == 0).all()
 
 
 # ---------------------------------------------------------------------------
