@@ -14,6 +14,10 @@ CPU oracle timed on a bounded row sample of the same workload.
 mode for short prefill: dense over each query's causal range, non-selected
 tokens masked); its roofline counts that dense work.
 
+--warmup-objective times the indexer's dense warm-up objective instead: the
+indexer scores, the target distribution (the main attention summed over the
+heads, dense) and the KL loss with its score gradient, in place.
+
 --bwd times the backward of the sparse attention over fixed indices
 (dsa_sparse_mla_attn_bwd: dq and dkv for an upstream gradient of the output)
 instead; the indices, output and lse come from one untimed forward pass.
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--workload", default="prefill32k")
     ap.add_argument("--bwd", action="store_true",
                     help="time the attention backward over fixed indices instead of the forward step")
+    ap.add_argument("--warmup-objective", action="store_true",
+                    help="time the indexer's dense warm-up objective (scores, target, KL) instead")
     ap.add_argument("--attn", choices=["sparse", "masked"], default="sparse",
                     help="attention stage: the sparse kernel, or the masked mode for short prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -164,6 +170,79 @@ def bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws,
     print(json.dumps(result))
 
 
+def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
+    """The dense warm-up objective per step: dsa_index_scores, dsa_warmup_target,
+    dsa_warmup_kl (gradient written over the scores)."""
+    import numpy as np
+    import torch
+    stream = torch.cuda.current_stream()
+    B, Lq, Lk = wl.batch, wl.q_len, wl.kv_len
+    target = torch.empty((B, Lq, Lk), dtype=torch.float32, device="cuda")
+    loss = torch.empty((B * Lq,), dtype=torch.float32, device="cuda")
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        dsa.dsa_warmup_target(prob, q, kv, target, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        dsa.dsa_warmup_kl(prob, scores, target, loss, scores, stream=stream)
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for ev in events:
+        step(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["index_scores", "warmup_target", "warmup_kl"]
+    per = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
+    pairs = wl.causal_pairs()
+    # algorithmic work: one evaluation of every head's scores per causal pair
+    # (the kernel evaluates them twice: once for the lse, once for the sum)
+    t_flop = 2.0 * wl.heads * wl.d_qk * pairs
+    k1_flop = 2.0 * wl.idx_heads * wl.idx_dim * pairs
+    kl_bytes = 16.0 * pairs  # scores read twice, target read once, gradient written
+    t_ms = float(np.mean(per["warmup_target"]))
+    kernels = {}
+    for n in names:
+        a = np.array(per[n])
+        kernels[n] = {"avg_ms": float(a.mean()), "median_ms": float(np.median(a)), "min_ms": float(a.min())}
+    kernels["index_scores"]["fp8_tflops"] = k1_flop / (kernels["index_scores"]["avg_ms"] * 1e-3) / 1e12
+    kernels["warmup_target"]["bf16_tflops"] = t_flop / (t_ms * 1e-3) / 1e12
+    kernels["warmup_kl"]["gbps"] = kl_bytes / (kernels["warmup_kl"]["avg_ms"] * 1e-3) / 1e9
+    tf = t_flop / (t_ms * 1e-3) / 1e12
+    result = {
+        "metric": "DSA indexer warm-up objective query tokens/s",
+        "value": B * Lq * args.steps / wall,
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "q_len": Lq, "kv_len": Lk, "heads": wl.heads,
+                   "d_latent": wl.d_latent, "d_rope": wl.d_rope, "idx_heads": wl.idx_heads,
+                   "idx_dim": wl.idx_dim, "pass": "dense warm-up objective"},
+        "kernels": kernels,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "kernel": "warmup_target", "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result))
+
+
 def traffic_for(kernel: str):
     """HBM bytes per launch from the committed PMC summary, if it was taken on the
     current kernel source; otherwise None."""
@@ -250,6 +329,9 @@ def main():
     aws = torch.empty(max(aws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    if args.warmup_objective:
+        bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w)
+        return
     if args.bwd:
         bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws, ws_bytes, aws,
                   aws_bytes, q_idx, k_idx, w)

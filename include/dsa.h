@@ -20,6 +20,11 @@
  *                        efficiency" table, KV-cache design).
  *   dsa_sparse_mla_attn_bwd  gradients of the sparse attention (dq, dkv) over
  *                        fixed indices, for the sparse training stage.
+ *   dsa_warmup_target    the main attention's distribution summed over the
+ *                        heads, dense over each query's causal range: the
+ *                        target of the indexer's warm-up objective.
+ *   dsa_warmup_kl        KL(target || softmax(indexer scores)) per query and
+ *                        its gradient with respect to the scores.
  *   dsa_masked_mha_attn  the same attention computed densely over each
  *                        query's causal range with the non-selected tokens
  *                        masked: the masked mode for short prefill.
@@ -203,6 +208,44 @@ int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint1
                             const int32_t* indices, const float* out, const float* lse,
                             const float* dout, float* dq, float* dkv, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * Target distribution of the indexer's dense warm-up, in which only the
+ * indexer is trained so that its softmax matches the main attention's
+ * distribution summed over the heads, under a KL loss (DeepSeek-V3.2 spec
+ * sheet, design overview and the curriculum row of its training table;
+ * lightning-indexer post, training section).  Readings: the main attention is
+ * dense over s <= pos(t), and the sum over heads is divided by H so that each
+ * row is a distribution:
+ *   target[b,t,s] = (1/H) sum_h softmax_s'(softmax_scale * q[b,t,h,:] . kv[b,s',:])[s]
+ * for s = 0 .. pos(t) (s < Lk); other entries are left untouched.
+ *
+ *   q, kv   as for dsa_sparse_mla_attn (topk is not used by this call)
+ *   target  [B, Lq, Lk] float32 output
+ * Scores are bf16 products with fp32 accumulation; exponentials in fp32.  The
+ * kernel computes each head's lse over the row first, so it reads the row's
+ * latents twice.  No workspace.
+ */
+int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* kv, float* target,
+                      void* stream);
+
+/*
+ * The warm-up's loss and score gradient (same passages): per query row, over
+ * s = 0 .. pos(t) (s < Lk), with pi = softmax(scores[b,t,:]),
+ *   loss[b,t]       = sum_s target (log target - log pi)   (terms with target = 0 are 0)
+ *   dscores[b,t,s]  = pi_s - target[b,t,s]                  (the gradient of sum_t loss)
+ * Entries of dscores past pos(t) are left untouched.
+ *
+ *   scores   [B, Lq, Lk] float32 (e.g. dsa_index_scores' output)
+ *   target   [B, Lq, Lk] float32 (e.g. dsa_warmup_target's output)
+ *   loss     [B, Lq]     float32 output
+ *   dscores  [B, Lq, Lk] float32 output; may be `scores` itself (in place),
+ *            must not overlap target or loss
+ * Only batch, q_len, kv_len and q_start of *p are used.  fp32 arithmetic,
+ * each row's loss summed in fp64.  No workspace.
+ */
+int dsa_warmup_kl(const dsa_problem* p, const float* scores, const float* target, float* loss,
+                  float* dscores, void* stream);
 
 /*
  * Masked mode for short prefill: the same attention as dsa_sparse_mla_attn,

@@ -81,8 +81,10 @@ def _load():
     L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_sparse_mla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp]
+    L.dsa_warmup_kl.argtypes = [P, vp, vp, vp, vp, vp]
     for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_masked_mha_attn,
-              L.dsa_sparse_mla_attn_bwd, L.dsa_forward):
+              L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_warmup_target, L.dsa_warmup_kl):
         f.restype = i32
     L.dsa_workspace_size.argtypes = [P, i32]
     L.dsa_workspace_size.restype = sz
@@ -160,6 +162,20 @@ def dsa_sparse_mla_attn_bwd(problem: Problem, q, kv, indices, out, lse, dout, dq
     _check(lib.dsa_sparse_mla_attn_bwd(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
                                        _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dkv),
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def dsa_warmup_target(problem: Problem, q, kv, target, stream=None) -> None:
+    """The warm-up target: the main attention's distribution summed over the heads
+    and divided by H, dense over s <= pos(t) (include/dsa.h: dsa_warmup_target)."""
+    _check(lib.dsa_warmup_target(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(target),
+                                 _stream(stream)))
+
+
+def dsa_warmup_kl(problem: Problem, scores, target, loss, dscores, stream=None) -> None:
+    """KL(target || softmax(scores)) per row and its score gradient
+    (include/dsa.h: dsa_warmup_kl); dscores may be scores itself."""
+    _check(lib.dsa_warmup_kl(ctypes.byref(problem.c()), _ptr(scores), _ptr(target), _ptr(loss),
+                             _ptr(dscores), _stream(stream)))
 
 
 def dsa_masked_mha_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:

@@ -58,8 +58,8 @@ int check_topk(const dsa_problem* p) {
   return DSA_OK;
 }
 
-int check_attn(const dsa_problem* p) {
-  if (int s = check_topk(p)) return s;
+// heads, latent shape and scale of the main attention (no top-k)
+int check_latent(const dsa_problem* p) {
   if (p->heads < 1 || p->d_latent < 1 || p->d_rope < 0)
     return fail(DSA_ERR_SHAPE, "heads, d_latent must be >= 1 and d_rope >= 0");
   if (!(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.0f))
@@ -78,6 +78,11 @@ int check_attn(const dsa_problem* p) {
                 "kv_len %d: the latent gather needs kv_len <= 2^24 and one sequence's cache "
                 "below 4 GiB - 8 KiB", p->kv_len);
   return DSA_OK;
+}
+
+int check_attn(const dsa_problem* p) {
+  if (int s = check_topk(p)) return s;
+  return check_latent(p);
 }
 
 // The backward's key lists name a (row, slot) pair as row * kpad + slot and
@@ -270,6 +275,38 @@ int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint1
   a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
   return hip_status(dsa::launch_sparse_mla_attn_bwd(a, workspace, (hipStream_t)stream),
                     "sparse_mla_attn_bwd launch");
+}
+
+int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* kv, float* target,
+                      void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_latent(p)) return s;
+  if (int s = check_ptr(q, "q", 16)) return s;
+  if (int s = check_ptr(kv, "kv", 16)) return s;
+  if (int s = check_ptr(target, "target", 4)) return s;
+  dsa::WarmupArgs a{};
+  a.q = q; a.kv = kv; a.target = target;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start; a.H = p->heads;
+  a.Dv = p->d_latent; a.Dr = p->d_rope;
+  a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;
+  a.inv_heads = 1.0f / (float)p->heads;
+  return hip_status(dsa::launch_warmup_target(a, (hipStream_t)stream), "warmup_target launch");
+}
+
+int dsa_warmup_kl(const dsa_problem* p, const float* scores, const float* target, float* loss,
+                  float* dscores, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_ptr(scores, "scores", 4)) return s;
+  if (int s = check_ptr(target, "target", 4)) return s;
+  if (int s = check_ptr(loss, "loss", 4)) return s;
+  if (int s = check_ptr(dscores, "dscores", 4)) return s;
+  if ((const void*)dscores == (const void*)target || (const void*)loss == (const void*)target ||
+      (const void*)loss == (const void*)scores || (const void*)loss == (const void*)dscores)
+    return fail(DSA_ERR_SHAPE, "warmup_kl: only dscores may share its buffer (with scores)");
+  dsa::WarmupArgs a{};
+  a.scores = scores; a.target = const_cast<float*>(target); a.loss = loss; a.dscores = dscores;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start;
+  return hip_status(dsa::launch_warmup_kl(a, (hipStream_t)stream), "warmup_kl launch");
 }
 
 int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,

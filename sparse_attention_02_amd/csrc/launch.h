@@ -73,6 +73,19 @@ struct AttnBwdArgs {
   float scale_log2;         // softmax_scale * log2(e)
 };
 
+// Dense warm-up objective of the indexer.
+struct WarmupArgs {
+  const uint16_t* q;       // [B, Lq, H, Dqk] bf16
+  const uint16_t* kv;      // [B, Lk, Dqk]    bf16
+  float* target;           // [B, Lq, Lk]     written for s <= pos(t)
+  const float* scores;     // [B, Lq, Lk]     indexer scores (KL kernel)
+  float* loss;             // [B, Lq]
+  float* dscores;          // [B, Lq, Lk]     written for s <= pos(t); may be `scores`
+  int B, Lq, Lk, q_start, H, Dv, Dr;
+  float scale_log2;        // softmax_scale * log2(e)
+  float inv_heads;         // 1 / H
+};
+
 // Launch `kernel(args...)` and return the launch's own status (not the
 // thread's sticky last-error state, which other libraries in the process also
 // write).  The argument types must match the kernel's parameters exactly.
@@ -98,5 +111,7 @@ int attn_splits(int rows, int k);
 hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& a, void* workspace, hipStream_t stream);
 size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int k, int dqk);
 size_t attn_workspace_bytes(int rows, int k, int H, int Dv);
+hipError_t launch_warmup_target(const WarmupArgs& a, hipStream_t stream);
+hipError_t launch_warmup_kl(const WarmupArgs& a, hipStream_t stream);
 
 }  // namespace dsa

@@ -1,0 +1,287 @@
+// Dense warm-up objective of the indexer (gfx950): only the indexer is
+// trained, so that its softmax over a query's scores matches the main
+// attention's distribution summed over the heads, under a KL loss
+// (DeepSeek-V3.2 spec sheet, design overview and the curriculum row of its
+// training table; lightning-indexer post, training section).
+//
+// Readings: the main attention is dense over s <= pos(t); the summed
+// distribution is divided by the head count, p[t,s] = (1/H) sum_h
+// softmax_s(z[t,h,s]) with z = scale * q . kv; a row's loss is
+// KL(p_t || softmax(I_t)) and its gradient with respect to the scores is
+// softmax(I_t) - p_t.
+//
+// Kernels:
+//  1. target (one block of 8 waves per row, 16 heads per wave): the row's
+//     causal keys stream through LDS in chunks of 32 contiguous latent rows;
+//     S = Q.K^T runs on bf16 MFMA with Q in registers, so a lane holds 4
+//     heads of one key.  Pass 1 keeps a running max and sum per lane and head
+//     and merges them over the 16 key lanes into the head's lse; pass 2
+//     recomputes S and sums exp(z - lse) over the heads (in lane, across the
+//     4 lane rows, then across the waves through LDS) into the target row.
+//  2. KL (one block per row, HBM-bound): online max / sum of the scores for
+//     log Z, then the loss and dI = exp(I - log Z) - p in one more read.
+#include <algorithm>
+
+#include "dsa_common.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kWChunk = 32;  // keys per chunk
+constexpr int kWWaves = 8;   // 8 waves x 16 heads = 128 heads
+
+template <int DQK>
+struct WShape {
+  static constexpr int DQKP = (DQK + 31) / 32 * 32;  // score width padded to K=32 steps
+  static constexpr int KST = DQKP / 32;
+  static constexpr int RS = DQKP * 2;                // LDS bytes per key row
+  static constexpr int PPR = RS / 16;                // 16-byte pieces per LDS row
+  static constexpr int RPR = DQK * 2 / 16;           // pieces present in the cache row
+  static constexpr bool SWZ = PPR % 8 == 0;
+  static constexpr int CHUNK_BYTES = kWChunk * RS;
+  static constexpr int BLOCKS = CHUNK_BYTES / 1024;  // 1 KB copies per chunk
+  static_assert(CHUNK_BYTES % 1024 == 0 && DQK % 8 == 0, "unsupported latent shape");
+};
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Keys s0 .. s0+31 (clamped to n - 1) of one sequence's cache -> LDS row r
+// at `dst`; piece lp of row r sits at physical piece lp ^ (r & 7) when the
+// row has a multiple of 8 pieces (conflict-free fragment reads).  Pad pieces
+// past the cache row re-read real ones (they meet zero q).  Each copy moves
+// 1 KB (lane i: bytes 16i..16i+15 of the block); waited for by the caller.
+template <typename S>
+__device__ __forceinline__ void load_chunk(uint8_t* dst, const uint8_t* seq, int s0, int n, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < (S::BLOCKS + kWWaves - 1) / kWWaves; ++j) {
+    const int blk = wave + kWWaves * j;
+    if (blk < S::BLOCKS) {
+      const int p = 64 * blk + lane;
+      const int r = p / S::PPR, pp = p % S::PPR;
+      const int lp = S::SWZ ? (pp ^ (r & 7)) : pp;
+      const int col = lp < S::RPR ? lp : lp - S::RPR;
+      const int key = min(s0 + r, n - 1);
+      const uint32_t off = (uint32_t)key * (uint32_t)(S::RPR * 16) + 16u * (uint32_t)col;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst + 1024 * blk));
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %2"
+                   :: "v"(off), "s"(m0), "s"(seq) : "memory", "m0");
+    }
+  }
+}
+
+// 16-lane (one MFMA lane row) exchanges
+__device__ __forceinline__ float xor_lanes(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <int DQK>
+__global__ __launch_bounds__(64 * kWWaves) void warmup_target_kernel(WarmupArgs a) {
+  using S = WShape<DQK>;
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][S::CHUNK_BYTES];
+  __shared__ float red[2][kWWaves][kWChunk];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, li = lane & 15;
+
+  // longest rows first (their blocks start earliest); rows go to the XCDs in
+  // runs of 32 consecutive rows, which stream the same keys
+  const int rows = a.B * a.Lq;
+  const int nb = (int)gridDim.x;
+  constexpr int kRun = 32;
+  const int full = nb / (8 * kRun) * (8 * kRun);
+  const int xi = (int)blockIdx.x >> 3;
+  const int lin = (int)blockIdx.x < full ? ((xi / kRun) * 8 + (int)(blockIdx.x & 7)) * kRun + xi % kRun
+                                         : (int)blockIdx.x;
+  const int bq = lin % a.B, tq = a.Lq - 1 - lin / a.B;  // batches interleaved, late positions first
+  const int row = bq * a.Lq + tq;
+  if (row >= rows) return;
+  const int n = min(a.q_start + tq + 1, a.Lk);  // keys 0 .. n-1
+  const int nch = (n + kWChunk - 1) / kWChunk;
+  const uint8_t* seq = (const uint8_t*)(a.kv + (size_t)bq * a.Lk * DQK);
+
+  // A operands: head 16 * wave + li, dims 32 ks + 8g .. +7 (zero past DQK or H)
+  v8bf qf[S::KST];
+  {
+    const int head = 16 * wave + li;
+    const uint16_t* qrow = a.q + ((size_t)row * a.H + min(head, a.H - 1)) * DQK;
+#pragma unroll
+    for (int ks = 0; ks < S::KST; ++ks) {
+      const int d0 = 32 * ks + 8 * g;
+      v4i v = {0, 0, 0, 0};
+      if (d0 < DQK && head < a.H) v = *(const v4i*)(qrow + d0);
+      qf[ks] = __builtin_bit_cast(v8bf, v);
+    }
+  }
+  bool hv[4];  // this lane's heads 16 * wave + 4g + r present
+#pragma unroll
+  for (int r = 0; r < 4; ++r) hv[r] = 16 * wave + 4 * g + r < a.H;
+
+  // S^T tile of chunk c: acc[kt][r] = q[head 4g + r] . kv[key 32c + 16 kt + li]
+  auto scores = [&](int st, v4f (&acc)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      acc[kt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      const int rr = 16 * kt + li;
+      const uint8_t* rowp = &kbuf[st][rr * S::RS];
+#pragma unroll
+      for (int ks = 0; ks < S::KST; ++ks) {
+        const int lp = 4 * ks + g;
+        const v8bf kf = __builtin_bit_cast(v8bf, *(const v4i*)(rowp + 16 * (S::SWZ ? (lp ^ (rr & 7)) : lp)));
+        acc[kt] = mfma_bf16_16x16x32(qf[ks], kf, acc[kt]);
+      }
+    }
+  };
+
+  // ---- pass 1: lse of every head over keys 0 .. n-1 (base 2)
+  float m[4], l[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) m[r] = -INFINITY, l[r] = 0.0f;
+  load_chunk<S>(kbuf[0], seq, 0, n, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int st = c & 1;
+    if (c + 1 < nch) load_chunk<S>(kbuf[st ^ 1], seq, kWChunk * (c + 1), n, wave, lane);
+    v4f acc[2];
+    scores(st, acc);
+    const bool ok0 = kWChunk * c + li < n, ok1 = kWChunk * c + 16 + li < n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x0 = ok0 ? acc[0][r] * a.scale_log2 : -INFINITY;
+      const float x1 = ok1 ? acc[1][r] * a.scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[r], fmaxf(x0, x1));
+      const float ms = mn == -INFINITY ? 0.0f : mn;  // nothing seen yet: every term is 0
+      l[r] = l[r] * fast_exp2(m[r] - ms) + fast_exp2(x0 - ms) + fast_exp2(x1 - ms);
+      m[r] = mn;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  float lse2[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mm = m[r], ll = l[r];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float mo = xor_lanes(mm, o), lo = xor_lanes(ll, o);
+      const float mn = fmaxf(mm, mo);
+      const float ms = mn == -INFINITY ? 0.0f : mn;
+      ll = ll * fast_exp2(mm - ms) + lo * fast_exp2(mo - ms);
+      mm = mn;
+    }
+    lse2[r] = mm + fast_log2(ll);  // key 0 is always present: finite for every head
+  }
+
+  // ---- pass 2: target[row, s] = (1/H) sum_h exp2(z * log2e - lse2[h])
+  float* trow = a.target + (size_t)row * a.Lk;
+  load_chunk<S>(kbuf[0], seq, 0, n, wave, lane);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int st = c & 1;
+    if (c + 1 < nch) load_chunk<S>(kbuf[st ^ 1], seq, kWChunk * (c + 1), n, wave, lane);
+    v4f acc[2];
+    scores(st, acc);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float s = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += hv[r] ? fast_exp2(fmaf(acc[kt][r], a.scale_log2, -lse2[r])) : 0.0f;
+      s += xor_lanes(s, 16);
+      s += xor_lanes(s, 32);
+      if (g == 0) red[st][wave][16 * kt + li] = s;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x < kWChunk) {
+      const int key = kWChunk * c + (int)threadIdx.x;
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWWaves; ++w) t += red[st][w][threadIdx.x];
+      if (key < n) trow[key] = t * a.inv_heads;
+    }
+  }
+}
+
+// ---- KL of a row and its score gradient
+template <int NT>
+__device__ __forceinline__ void block_max_sum(float& m, float& l, float* sm, float* sl) {
+  // merge (max, sum of exp(x - max)) pairs over the block (natural exp)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float mo = __shfl_xor(m, o, 64), lo = __shfl_xor(l, o, 64);
+    const float mn = fmaxf(m, mo);
+    const float ms = mn == -INFINITY ? 0.0f : mn;
+    l = l * __expf(m - ms) + lo * __expf(mo - ms);
+    m = mn;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) sm[wave] = m, sl[wave] = l;
+  __syncthreads();
+  m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) m = fmaxf(m, sm[w]);
+  const float ms = m == -INFINITY ? 0.0f : m;
+  l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) l += sl[w] * __expf(sm[w] - ms);
+  __syncthreads();
+}
+
+constexpr int kKlThreads = 256;
+
+__global__ __launch_bounds__(kKlThreads) void warmup_kl_kernel(WarmupArgs a) {
+  __shared__ float sm[kKlThreads / 64], sl[kKlThreads / 64];
+  __shared__ double sd[kKlThreads / 64];
+  const int row = blockIdx.x;
+  const int t = row % a.Lq;
+  const int n = min(a.q_start + t + 1, a.Lk);
+  const float* I = a.scores + (size_t)row * a.Lk;
+  const float* P = a.target + (size_t)row * a.Lk;
+  float* D = a.dscores + (size_t)row * a.Lk;
+  // online max / sum over the row (4 entries per thread per step where aligned)
+  float m = -INFINITY, l = 0.0f;
+  for (int s = threadIdx.x; s < n; s += kKlThreads) {
+    const float x = I[s];
+    const float mn = fmaxf(m, x);
+    l = l * __expf(m - mn) + __expf(x - mn);
+    m = mn;
+  }
+  block_max_sum<kKlThreads>(m, l, sm, sl);
+  const float logz = m + __logf(l);
+  double loss = 0.0;
+  for (int s = threadIdx.x; s < n; s += kKlThreads) {
+    const float lp = I[s] - logz;  // log softmax
+    const float p = P[s];
+    if (p > 0.0f) loss += (double)p * ((double)__logf(p) - (double)lp);
+    D[s] = __expf(lp) - p;  // the same thread read I[s] above: in place is safe
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) loss += __shfl_xor(loss, o, 64);
+  if ((threadIdx.x & 63) == 0) sd[threadIdx.x >> 6] = loss;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
+#pragma unroll
+    for (int w = 0; w < kKlThreads / 64; ++w) tot += sd[w];
+    a.loss[row] = (float)tot;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_warmup_target(const WarmupArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)a.B * a.Lq)), block(64 * kWWaves);
+  if (a.Dv == 512 && a.Dr == 64) return launch_kernel((const void*)warmup_target_kernel<576>, grid, block, 0, stream, a);
+  if (a.Dv == 64 && a.Dr == 16) return launch_kernel((const void*)warmup_target_kernel<80>, grid, block, 0, stream, a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_warmup_kl(const WarmupArgs& a, hipStream_t stream) {
+  return launch_kernel((const void*)warmup_kl_kernel, dim3((unsigned)((long long)a.B * a.Lq)), dim3(kKlThreads), 0,
+                       stream, a);
+}
+
+}  // namespace dsa

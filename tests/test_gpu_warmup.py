@@ -1,0 +1,151 @@
+"""GPU parity of the dense warm-up objective (target distribution, KL loss and
+its score gradient) against the CPU oracle in double precision.
+
+Bars, from the arithmetic: the target's scores are bf16 products summed in
+fp32 and its exponentials are fp32 (relative error ~1e-6 on each head's
+probabilities, a little more on rows with large dot products), so the target
+is compared per element within 2e-6 + 2e-4 * |reference|.  The KL kernel gets
+the oracle's own fp32 inputs.  Its log softmax, I - log Z, is rounded at the
+scale of the row's largest score M (about 3 * 2^-24 * M absolute, log Z
+included), which moves each gradient entry by that much times pi <= 1 and
+the loss by that much in all: both are checked within 1e-6 + 4e-7 * M."""
+import numpy as np
+import pytest
+import torch
+
+import dsa_inputs
+import oracle
+from gpu_util import Inputs, dev, log, run_stages
+from test_gpu_parity import EDGE
+
+pytestmark = pytest.mark.gpu
+
+T_ATOL, T_RTOL = 2e-6, 2e-4
+KL_ATOL, KL_PER_SCORE = 1e-6, 4e-7
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_02_amd as m
+    return m
+
+
+def _wl(name):
+    return dsa_inputs.WORKLOADS[name] if name in dsa_inputs.WORKLOADS else EDGE[name]
+
+
+def _target_gpu(dsa, wl, d):
+    prob = dsa.Problem.from_workload(wl)
+    t = torch.full((wl.batch, wl.q_len, wl.kv_len), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_warmup_target(prob, d["q"], d["kv"], t)
+    torch.cuda.synchronize()
+    return t.reshape(wl.batch * wl.q_len, wl.kv_len).cpu().numpy()
+
+
+def _check_target(label, got, ref, pos, Lk):
+    for i in range(got.shape[0]):
+        n = min(int(pos[i]) + 1, Lk)
+        err = np.abs(got[i, :n] - ref[i, :n])
+        assert (err <= T_ATOL + T_RTOL * np.abs(ref[i, :n])).all(), \
+            f"{label} row {i}: max err {err.max():.3e}"
+        assert np.isnan(got[i, n:]).all(), f"{label} row {i}: entries past pos(t) written"
+        assert abs(float(got[i, :n].astype(np.float64).sum()) - 1.0) < 1e-4
+    rel = np.nanmax(np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30))
+    log(f"[{label}] target max relative error {rel:.2e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "mla_small", "k_above_len", "few_queries"])
+def test_target_matches_oracle(dsa, name):
+    wl = _wl(name)
+    inp = Inputs.make(wl)
+    got = _target_gpu(dsa, wl, inp.device())
+    R = wl.batch * wl.q_len
+    rb, pos = dsa_inputs.row_batch_pos(wl, np.arange(R))
+    ref = oracle.warmup_target(inp.kv, inp.q.reshape(R, wl.heads, -1), rb, pos, wl.softmax_scale)
+    _check_target(wl.name, got, ref, pos, wl.kv_len)
+
+
+def test_target_prefill4k_sampled_rows(dsa):
+    wl = dsa_inputs.WORKLOADS["prefill4k"]
+    inp = Inputs.make(wl)
+    got = _target_gpu(dsa, wl, inp.device())
+    rows = dsa_inputs.sample_rows(wl, 10)
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    R = wl.batch * wl.q_len
+    ref = oracle.warmup_target(inp.kv, inp.q.reshape(R, wl.heads, -1)[rows], rb, pos, wl.softmax_scale)
+    _check_target("prefill4k", got[rows], ref, pos, wl.kv_len)
+
+
+def _kl_case(wl):
+    """Oracle-made fp32 scores and target for every row of the workload."""
+    inp = Inputs.make(wl)
+    R = wl.batch * wl.q_len
+    rows = np.arange(R)
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    I = oracle.index_scores(inp.k_idx, inp.q_idx.reshape(R, wl.idx_heads, -1), inp.w.reshape(R, -1), rb, pos,
+                            fill=np.nan).astype(np.float32)
+    P = oracle.warmup_target(inp.kv, inp.q.reshape(R, wl.heads, -1), rb, pos, wl.softmax_scale).astype(np.float32)
+    return inp, I, P, pos
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "few_queries"])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_kl_matches_oracle(dsa, name, in_place):
+    wl = _wl(name)
+    _, I, P, pos = _kl_case(wl)
+    R = wl.batch * wl.q_len
+    loss_or, d_or = oracle.warmup_kl(I, P, pos)
+    prob = dsa.Problem.from_workload(wl)
+    sc = dev(I)
+    tg = dev(P)
+    loss = torch.full((R,), float("nan"), dtype=torch.float32, device="cuda")
+    ds = sc if in_place else torch.full_like(sc, float("nan"))
+    dsa.dsa_warmup_kl(prob, sc, tg, loss, ds)
+    torch.cuda.synchronize()
+    d = ds.cpu().numpy()
+    l = loss.cpu().numpy()
+    for i in range(R):
+        n = min(int(pos[i]) + 1, wl.kv_len)
+        bound = KL_ATOL + KL_PER_SCORE * float(np.abs(I[i, :n]).max())
+        assert np.abs(d[i, :n] - d_or[i, :n]).max() <= bound, f"row {i}"
+        assert abs(float(l[i]) - loss_or[i]) <= bound + 1e-5 * loss_or[i], f"loss row {i}"
+        if not in_place:
+            assert np.isnan(d[i, n:]).all()
+    log(f"[{wl.name} kl{' in place' if in_place else ''}] loss max rel "
+        f"{np.max(np.abs(l - loss_or) / np.maximum(loss_or, 1e-30)):.2e}, "
+        f"dscores max abs {np.nanmax(np.abs(d - d_or)):.2e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill4k"])
+def test_warmup_chain_indexer_target_kl(dsa, name):
+    """The warm-up objective end to end on the GPU (indexer scores, target, KL in
+    place) against the oracle's chain, on sampled rows."""
+    wl = dsa_inputs.WORKLOADS[name]
+    inp = Inputs.make(wl)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
+    scores, _, _, _ = run_stages(prob, d, wl)
+    target = torch.empty_like(scores)
+    dsa.dsa_warmup_target(prob, d["q"], d["kv"], target)
+    loss = torch.empty((wl.batch * wl.q_len,), dtype=torch.float32, device="cuda")
+    dsa.dsa_warmup_kl(prob, scores, target, loss, scores)
+    torch.cuda.synchronize()
+    R = wl.batch * wl.q_len
+    rows = np.arange(R) if R <= 512 else dsa_inputs.sample_rows(wl, 10)
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    I = oracle.index_scores(inp.k_idx, inp.q_idx.reshape(R, wl.idx_heads, -1)[rows], inp.w.reshape(R, -1)[rows],
+                            rb, pos, fill=np.nan).astype(np.float32)
+    P = oracle.warmup_target(inp.kv, inp.q.reshape(R, wl.heads, -1)[rows], rb, pos, wl.softmax_scale)
+    loss_or, d_or = oracle.warmup_kl(I, P.astype(np.float32), pos)
+    got_d = scores.reshape(R, wl.kv_len).cpu().numpy()[rows]
+    got_l = loss.cpu().numpy()[rows]
+    err_d = max(np.abs(got_d[i, : p + 1] - d_or[i, : p + 1]).max() for i, p in enumerate(pos))
+    # the GPU target differs from the oracle's by <= T_RTOL relative: that moves
+    # the gradient by as much and the loss by about T_RTOL * (1 + |log ratio|),
+    # on top of the KL kernel's own rounding
+    assert err_d <= 5e-5 + KL_PER_SCORE * float(np.nanmax(np.abs(I))), err_d
+    np.testing.assert_allclose(got_l, loss_or, rtol=5e-3, atol=1e-5)
+    log(f"[{name} chain] dscores max abs {err_d:.2e}, loss max rel "
+        f"{np.max(np.abs(got_l - loss_or) / np.maximum(loss_or, 1e-30)):.2e}")
