@@ -153,6 +153,28 @@ def test_backward_checks():
     assert s == -2
 
 
+def test_warmup_checks():
+    # the target needs the attention's latent shape but not a valid topk
+    p = Problem(**{**GOOD.__dict__, "topk": 0})
+    s, msg = _status(dsa.dsa_warmup_target, p, None, FAKE, FAKE, stream=0)
+    assert s == -1 and "q" in msg
+    s, _ = _status(dsa.dsa_warmup_target, Problem(**{**GOOD.__dict__, "d_latent": 128}), FAKE, FAKE, FAKE,
+                   stream=0)
+    assert s == -3
+    s, msg = _status(dsa.dsa_warmup_target, GOOD, FAKE, FAKE, FAKE + 2, stream=0)
+    assert s == -5 and "target" in msg
+    s, _ = _status(dsa.dsa_warmup_target, Problem(**{**GOOD.__dict__, "q_start": 1}), FAKE, FAKE, FAKE,
+                   stream=0)
+    assert s == -2
+    # the KL: only dscores may share a buffer, and only with the scores
+    other = FAKE + (1 << 20)
+    for args in [(FAKE, FAKE, other, FAKE), (FAKE, other, FAKE, other + 256), (FAKE, other, other + 256, other + 256)]:
+        s, msg = _status(dsa.dsa_warmup_kl, GOOD, *args, stream=0)
+        assert s == -2, msg
+    s, msg = _status(dsa.dsa_warmup_kl, GOOD, FAKE, FAKE + 256, None, FAKE, stream=0)
+    assert s == -1 and "loss" in msg
+
+
 def test_workspace_sizes_and_forward_checks():
     assert dsa.workspace_size(GOOD, dsa.DSA_OP_INDEX_SCORES) == 0
     assert dsa.workspace_size(GOOD, dsa.DSA_OP_TOPK) == 0
