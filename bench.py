@@ -14,9 +14,10 @@ CPU oracle timed on a bounded row sample of the same workload.
 mode for short prefill: dense over each query's causal range, non-selected
 tokens masked); its roofline counts that dense work.
 
---warmup-objective times the indexer's dense warm-up objective instead: the
+--warmup-objective times the indexer's dense warm-up step instead: the
 indexer scores, the target distribution (the main attention summed over the
-heads, dense) and the KL loss with its score gradient, in place.
+heads, dense), the KL loss with its score gradient (in place), and the
+gradients into the indexer's q_I, w and k_I.
 
 --bwd times the backward of the sparse attention over fixed indices
 (dsa_sparse_mla_attn_bwd: dq and dkv for an upstream gradient of the output)
@@ -179,8 +180,12 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
     B, Lq, Lk = wl.batch, wl.q_len, wl.kv_len
     target = torch.empty((B, Lq, Lk), dtype=torch.float32, device="cuda")
     loss = torch.empty((B * Lq,), dtype=torch.float32, device="cuda")
+    dq_idx = torch.empty((B, Lq, wl.idx_heads, wl.idx_dim), dtype=torch.float32, device="cuda")
+    dw = torch.empty((B, Lq, wl.idx_heads), dtype=torch.float32, device="cuda")
+    dk_idx = torch.empty((B, Lk, wl.idx_dim), dtype=torch.float32, device="cuda")
 
     def step(ev=None):
+        dk_idx.zero_()  # accumulated into by the indexer backward
         if ev:
             ev[0].record(stream)
         dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
@@ -192,17 +197,20 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
         dsa.dsa_warmup_kl(prob, scores, target, loss, scores, stream=stream)
         if ev:
             ev[3].record(stream)
+        dsa.dsa_index_scores_bwd(prob, q_idx, k_idx, w, scores, dq_idx, dw, dk_idx, stream=stream)
+        if ev:
+            ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for ev in events:
         step(ev)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    names = ["index_scores", "warmup_target", "warmup_kl"]
+    names = ["index_scores", "warmup_target", "warmup_kl", "index_scores_bwd"]
     per = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
     pairs = wl.causal_pairs()
     # algorithmic work: one evaluation of every head's scores per causal pair
@@ -218,6 +226,10 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
     kernels["index_scores"]["fp8_tflops"] = k1_flop / (kernels["index_scores"]["avg_ms"] * 1e-3) / 1e12
     kernels["warmup_target"]["bf16_tflops"] = t_flop / (t_ms * 1e-3) / 1e12
     kernels["warmup_kl"]["gbps"] = kl_bytes / (kernels["warmup_kl"]["avg_ms"] * 1e-3) / 1e9
+    # indexer backward: u once plus the dq_I and dk_I products, 3 * 2 * H_I * d_I
+    # per causal pair (the two kernels each recompute u: 4 evaluations run)
+    ib_flop = 3.0 * k1_flop
+    kernels["index_scores_bwd"]["bf16_tflops"] = ib_flop / (kernels["index_scores_bwd"]["avg_ms"] * 1e-3) / 1e12
     tf = t_flop / (t_ms * 1e-3) / 1e12
     result = {
         "metric": "DSA indexer warm-up objective query tokens/s",
@@ -234,7 +246,7 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "q_len": Lq, "kv_len": Lk, "heads": wl.heads,
                    "d_latent": wl.d_latent, "d_rope": wl.d_rope, "idx_heads": wl.idx_heads,
-                   "idx_dim": wl.idx_dim, "pass": "dense warm-up objective"},
+                   "idx_dim": wl.idx_dim, "pass": "dense warm-up step (objective and indexer gradients)"},
         "kernels": kernels,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "kernel": "warmup_target", "traffic": None},

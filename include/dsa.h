@@ -25,6 +25,8 @@
  *                        target of the indexer's warm-up objective.
  *   dsa_warmup_kl        KL(target || softmax(indexer scores)) per query and
  *                        its gradient with respect to the scores.
+ *   dsa_index_scores_bwd gradients of the indexer scores with respect to the
+ *                        indexer's q_I, w and k_I.
  *   dsa_masked_mha_attn  the same attention computed densely over each
  *                        query's causal range with the non-selected tokens
  *                        masked: the masked mode for short prefill.
@@ -246,6 +248,30 @@ int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* k
  */
 int dsa_warmup_kl(const dsa_problem* p, const float* scores, const float* target, float* loss,
                   float* dscores, void* stream);
+
+/*
+ * Gradients of dsa_index_scores with respect to its inputs, for a gradient
+ * dscores of the scores (e.g. dsa_warmup_kl's): the indexer's backward in its
+ * warm-up training (same passages as dsa_warmup_target).  With
+ * u = q_I[b,t,j,:] . k_I[b,s,:] and the ReLU's derivative taken as 0 at 0,
+ * summed over s = 0 .. pos(t) (s < Lk):
+ *   dw[b,t,j]       = sum_s dscores[b,t,s] ReLU(u)
+ *   dq_idx[b,t,j,:] = w[b,t,j] sum_s dscores[b,t,s] [u > 0] k_I[b,s,:]
+ *   dk_idx[b,s,:]  += sum_(t,j) dscores[b,t,s] w[b,t,j] [u > 0] q_I[b,t,j,:]
+ *
+ *   q_idx, k_idx, w  as for dsa_index_scores
+ *   dscores  [B, Lq, Lk] float32; entries past pos(t) are not read
+ *   dq_idx   [B, Lq, H_I, d_I] float32 output (written)
+ *   dw       [B, Lq, H_I] float32 output (written)
+ *   dk_idx   [B, Lk, d_I] float32, ACCUMULATED into (fp32 atomic adds of
+ *            per-block partial sums: the caller zeroes it; the last bits can
+ *            vary between runs)
+ * u is recomputed on bf16 matrix cores (the e4m3 values are exact in bf16)
+ * with fp32 accumulation; dscores * w is rounded to bf16 for the two
+ * products; dw is accumulated in fp32.  No workspace.
+ */
+int dsa_index_scores_bwd(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                         const float* dscores, float* dq_idx, float* dw, float* dk_idx, void* stream);
 
 /*
  * Masked mode for short prefill: the same attention as dsa_sparse_mla_attn,

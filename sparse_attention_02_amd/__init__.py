@@ -83,8 +83,10 @@ def _load():
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp]
     L.dsa_warmup_kl.argtypes = [P, vp, vp, vp, vp, vp]
+    L.dsa_index_scores_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_masked_mha_attn,
-              L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_warmup_target, L.dsa_warmup_kl):
+              L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_warmup_target, L.dsa_warmup_kl,
+              L.dsa_index_scores_bwd):
         f.restype = i32
     L.dsa_workspace_size.argtypes = [P, i32]
     L.dsa_workspace_size.restype = sz
@@ -176,6 +178,14 @@ def dsa_warmup_kl(problem: Problem, scores, target, loss, dscores, stream=None) 
     (include/dsa.h: dsa_warmup_kl); dscores may be scores itself."""
     _check(lib.dsa_warmup_kl(ctypes.byref(problem.c()), _ptr(scores), _ptr(target), _ptr(loss),
                              _ptr(dscores), _stream(stream)))
+
+
+def dsa_index_scores_bwd(problem: Problem, q_idx, k_idx, w, dscores, dq_idx, dw, dk_idx, stream=None) -> None:
+    """Gradients of the indexer scores with respect to q_I, w (written) and k_I
+    (accumulated into) for a score gradient dscores
+    (include/dsa.h: dsa_index_scores_bwd)."""
+    _check(lib.dsa_index_scores_bwd(ctypes.byref(problem.c()), _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(dscores),
+                                    _ptr(dq_idx), _ptr(dw), _ptr(dk_idx), _stream(stream)))
 
 
 def dsa_masked_mha_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:

@@ -309,6 +309,25 @@ int dsa_warmup_kl(const dsa_problem* p, const float* scores, const float* target
   return hip_status(dsa::launch_warmup_kl(a, (hipStream_t)stream), "warmup_kl launch");
 }
 
+int dsa_index_scores_bwd(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                         const float* dscores, float* dq_idx, float* dw, float* dk_idx, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_index(p)) return s;
+  if (int s = check_ptr(q_idx, "q_idx", 16)) return s;
+  if (int s = check_ptr(k_idx, "k_idx", 16)) return s;
+  if (int s = check_ptr(w, "w", 4)) return s;
+  if (int s = check_ptr(dscores, "dscores", 4)) return s;
+  if (int s = check_ptr(dq_idx, "dq_idx", 16)) return s;
+  if (int s = check_ptr(dw, "dw", 4)) return s;
+  if (int s = check_ptr(dk_idx, "dk_idx", 16)) return s;
+  dsa::IndexBwdArgs a{};
+  a.q_idx = q_idx; a.k_idx = k_idx; a.w = w; a.dscores = dscores;
+  a.dq_idx = dq_idx; a.dw = dw; a.dk_idx = dk_idx;
+  a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start;
+  a.H = p->idx_heads; a.DI = p->idx_dim;
+  return hip_status(dsa::launch_index_scores_bwd(a, (hipStream_t)stream), "index_scores_bwd launch");
+}
+
 int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
                         const int32_t* indices, float* out, float* lse, void* stream) {
   if (int s = check_common(p)) return s;

@@ -86,6 +86,18 @@ struct WarmupArgs {
   float inv_heads;         // 1 / H
 };
 
+// Gradients of the indexer scores with respect to q_I, w and k_I.
+struct IndexBwdArgs {
+  const uint8_t* q_idx;    // [B, Lq, H_I, d_I] e4m3fn
+  const uint8_t* k_idx;    // [B, Lk, d_I]      e4m3fn
+  const float* w;          // [B, Lq, H_I]
+  const float* dscores;    // [B, Lq, Lk]       read for s <= pos(t)
+  float* dq_idx;           // [B, Lq, H_I, d_I] written
+  float* dw;               // [B, Lq, H_I]      written
+  float* dk_idx;           // [B, Lk, d_I]      accumulated into
+  int B, Lq, Lk, q_start, H, DI;
+};
+
 // Launch `kernel(args...)` and return the launch's own status (not the
 // thread's sticky last-error state, which other libraries in the process also
 // write).  The argument types must match the kernel's parameters exactly.
@@ -113,5 +125,6 @@ size_t attn_bwd_workspace_bytes(int B, int Lq, int Lk, int k, int dqk);
 size_t attn_workspace_bytes(int rows, int k, int H, int Dv);
 hipError_t launch_warmup_target(const WarmupArgs& a, hipStream_t stream);
 hipError_t launch_warmup_kl(const WarmupArgs& a, hipStream_t stream);
+hipError_t launch_index_scores_bwd(const IndexBwdArgs& a, hipStream_t stream);
 
 }  // namespace dsa

@@ -149,3 +149,57 @@ def test_warmup_chain_indexer_target_kl(dsa, name):
     np.testing.assert_allclose(got_l, loss_or, rtol=5e-3, atol=1e-5)
     log(f"[{name} chain] dscores max abs {err_d:.2e}, loss max rel "
         f"{np.max(np.abs(got_l - loss_or) / np.maximum(loss_or, 1e-30)):.2e}")
+
+
+# ---------------------------------------------------------------------------
+# Gradients of the indexer scores with respect to q_I, w and k_I
+# ---------------------------------------------------------------------------
+
+IB_TOL = 1e-2  # dq_I, dk_I: dscores * w is rounded to bf16 (2^-9) for the products
+DW_TOL = 1e-5  # dw: fp32 sums of exact ReLU(u) times fp32 dscores
+
+
+def _ib_check(label, got, ref, tol):
+    err = float(np.abs(got - ref).max())
+    scale = float(np.abs(ref).max())
+    log(f"[{label}] max-abs {err:.3e} of max|ref| {scale:.3e} (relative {err / max(scale, 1e-30):.2e})")
+    assert err <= tol * scale + 1e-7, f"{label}: {err} > {tol} * {scale}"
+
+
+def _index_bwd_case(dsa, wl, rows=None, seed=5):
+    inp = Inputs.make(wl)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
+    R = wl.batch * wl.q_len
+    rb_all, pos_all = dsa_inputs.row_batch_pos(wl, np.arange(R))
+    rng = np.random.default_rng(seed)
+    g = rng.normal(size=(R, wl.kv_len)).astype(np.float32)
+    g[np.arange(wl.kv_len)[None, :] > pos_all[:, None]] = np.nan  # never read
+    sel = np.arange(R) if rows is None else np.asarray(rows)
+    if rows is not None:
+        keep = np.zeros(R, bool)
+        keep[sel] = True
+        g[~keep] = np.where(np.isnan(g[~keep]), np.nan, 0.0)
+    dq = torch.full((wl.batch, wl.q_len, wl.idx_heads, wl.idx_dim), float("nan"), dtype=torch.float32, device="cuda")
+    dw = torch.full((wl.batch, wl.q_len, wl.idx_heads), float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((wl.batch, wl.kv_len, wl.idx_dim), dtype=torch.float32, device="cuda")
+    dsa.dsa_index_scores_bwd(prob, d["q_idx"], d["k_idx"], d["w"], dev(g), dq, dw, dk)
+    torch.cuda.synchronize()
+    rb, pos = rb_all[sel], pos_all[sel]
+    dq_or, dw_or, dk_or = oracle.index_scores_bwd(inp.k_idx, inp.q_idx.reshape(R, wl.idx_heads, -1)[sel],
+                                                  inp.w.reshape(R, -1)[sel], rb, pos,
+                                                  np.nan_to_num(g[sel].astype(np.float64), nan=0.0))
+    _ib_check(f"{wl.name} dq_I", dq.reshape(R, wl.idx_heads, -1).cpu().numpy()[sel], dq_or, IB_TOL)
+    _ib_check(f"{wl.name} dw", dw.reshape(R, -1).cpu().numpy()[sel], dw_or, DW_TOL)
+    _ib_check(f"{wl.name} dk_I", dk.cpu().numpy(), dk_or, IB_TOL)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "few_queries", "mla_small", "k_above_len", "wide_indexer",
+                                  "decode_small"])
+def test_index_scores_bwd_matches_oracle(dsa, name):
+    _index_bwd_case(dsa, _wl(name))
+
+
+def test_index_scores_bwd_prefill4k_sampled_rows(dsa):
+    wl = dsa_inputs.WORKLOADS["prefill4k"]
+    _index_bwd_case(dsa, wl, rows=dsa_inputs.sample_rows(wl, 6))
