@@ -11,10 +11,10 @@
 // softmax(I_t) - p_t.
 //
 // Kernels:
-//  1. target (one block of 8 waves per row, 16 heads per wave): the row's
-//     causal keys stream through LDS in chunks of 32 contiguous latent rows;
-//     S = Q.K^T runs on bf16 MFMA with Q in registers, so a lane holds 4
-//     heads of one key.  Pass 1 keeps a running max and sum per lane and head
+//  1. target (one block of 8 waves per two adjacent rows, 32 heads per
+//     wave): the rows' causal keys stream through LDS in chunks of 32
+//     contiguous latent rows; S = Q.K^T runs on bf16 MFMA with Q in
+//     registers, so a lane holds 4 heads of one key.  Pass 1 keeps a running max and sum per lane and head
 //     and merges them over the 16 key lanes into the head's lse; pass 2
 //     recomputes S and sums exp(z - lse) over the heads (in lane, across the
 //     4 lane rows, then across the waves through LDS) into the target row.
@@ -30,7 +30,7 @@ namespace dsa {
 namespace {
 
 constexpr int kWChunk = 32;  // keys per chunk
-constexpr int kWWaves = 8;   // 8 waves x 16 heads = 128 heads
+constexpr int kWWaves = 8;   // 2 rows x 4 waves x 32 heads
 
 template <int DQK>
 struct WShape {
@@ -76,131 +76,159 @@ __device__ __forceinline__ void load_chunk(uint8_t* dst, const uint8_t* seq, int
 // 16-lane (one MFMA lane row) exchanges
 __device__ __forceinline__ float xor_lanes(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// Two adjacent query rows per block (their causal ranges differ by one key):
+// waves 0-3 take row t0, waves 4-7 row t0 + 1, each wave 32 heads (2 tiles),
+// so every K fragment read from LDS feeds two MFMAs.
+constexpr int kWRows = 2;
+constexpr int kWHt = 2;  // 16-head tiles per wave
+
 template <int DQK>
 __global__ __launch_bounds__(64 * kWWaves) void warmup_target_kernel(WarmupArgs a) {
   using S = WShape<DQK>;
+  constexpr int WPR = kWWaves / kWRows;  // waves per row
   __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][S::CHUNK_BYTES];
   __shared__ float red[2][kWWaves][kWChunk];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
+  const int rr = wave / WPR, hg = wave % WPR;
 
-  // longest rows first (their blocks start earliest); rows go to the XCDs in
-  // runs of 32 consecutive rows, which stream the same keys
-  const int rows = a.B * a.Lq;
+  // longest row pairs first (their blocks start earliest); pairs go to the
+  // XCDs in runs of 32 consecutive pairs, which stream the same keys
+  const int pairs = (a.Lq + kWRows - 1) / kWRows;
   const int nb = (int)gridDim.x;
   constexpr int kRun = 32;
   const int full = nb / (8 * kRun) * (8 * kRun);
   const int xi = (int)blockIdx.x >> 3;
   const int lin = (int)blockIdx.x < full ? ((xi / kRun) * 8 + (int)(blockIdx.x & 7)) * kRun + xi % kRun
                                          : (int)blockIdx.x;
-  const int bq = lin % a.B, tq = a.Lq - 1 - lin / a.B;  // batches interleaved, late positions first
-  const int row = bq * a.Lq + tq;
-  if (row >= rows) return;
-  const int n = min(a.q_start + tq + 1, a.Lk);  // keys 0 .. n-1
-  const int nch = (n + kWChunk - 1) / kWChunk;
+  const int bq = lin % a.B, t0 = kWRows * (pairs - 1 - lin / a.B);  // batches interleaved, late pairs first
+  const int t = t0 + rr;
+  const bool row_ok = t < a.Lq;  // wave-uniform
+  const size_t row = (size_t)bq * a.Lq + (row_ok ? t : t0);
+  const int n = min(a.q_start + t + 1, a.Lk);                          // this wave's keys 0 .. n-1
+  const int n_max = min(a.q_start + min(t0 + kWRows, a.Lq), a.Lk);     // the block's longest row
+  const int nch = (n_max + kWChunk - 1) / kWChunk;
   const uint8_t* seq = (const uint8_t*)(a.kv + (size_t)bq * a.Lk * DQK);
 
-  // A operands: head 16 * wave + li, dims 32 ks + 8g .. +7 (zero past DQK or H)
-  v8bf qf[S::KST];
-  {
-    const int head = 16 * wave + li;
-    const uint16_t* qrow = a.q + ((size_t)row * a.H + min(head, a.H - 1)) * DQK;
+  // B operands: head 32 hg + 16 ht + li, dims 32 ks + 8g .. +7 (zero past DQK or H)
+  v8bf qf[kWHt][S::KST];
+  bool hv[kWHt][4];  // this lane's heads 32 hg + 16 ht + 4g + r present
+#pragma unroll
+  for (int ht = 0; ht < kWHt; ++ht) {
+    const int head = 32 * hg + 16 * ht + li;
+    const bool ok = row_ok && head < a.H;
+    const uint16_t* qrow = a.q + (row * a.H + min(head, a.H - 1)) * DQK;
 #pragma unroll
     for (int ks = 0; ks < S::KST; ++ks) {
       const int d0 = 32 * ks + 8 * g;
       v4i v = {0, 0, 0, 0};
-      if (d0 < DQK && head < a.H) v = *(const v4i*)(qrow + d0);
-      qf[ks] = __builtin_bit_cast(v8bf, v);
+      if (d0 < DQK && ok) v = *(const v4i*)(qrow + d0);
+      qf[ht][ks] = __builtin_bit_cast(v8bf, v);
     }
-  }
-  bool hv[4];  // this lane's heads 16 * wave + 4g + r present
 #pragma unroll
-  for (int r = 0; r < 4; ++r) hv[r] = 16 * wave + 4 * g + r < a.H;
+    for (int r = 0; r < 4; ++r) hv[ht][r] = row_ok && 32 * hg + 16 * ht + 4 * g + r < a.H;
+  }
 
-  // S^T tile of chunk c: acc[kt][r] = q[head 4g + r] . kv[key 32c + 16 kt + li]
-  auto scores = [&](int st, v4f (&acc)[2]) {
+  // S tiles of chunk c: acc[ht][kt][r] = q[head 16ht + 4g + r] . kv[key 32c + 16kt + li]
+  auto scores = [&](int st, v4f (&acc)[kWHt][2]) {
+#pragma unroll
+    for (int ht = 0; ht < kWHt; ++ht)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[ht][kt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      acc[kt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-      const int rr = 16 * kt + li;
-      const uint8_t* rowp = &kbuf[st][rr * S::RS];
+      const int kr = 16 * kt + li;
+      const uint8_t* rowp = &kbuf[st][kr * S::RS];
 #pragma unroll
       for (int ks = 0; ks < S::KST; ++ks) {
         const int lp = 4 * ks + g;
-        const v8bf kf = __builtin_bit_cast(v8bf, *(const v4i*)(rowp + 16 * (S::SWZ ? (lp ^ (rr & 7)) : lp)));
-        acc[kt] = mfma_bf16_16x16x32(qf[ks], kf, acc[kt]);
+        const v8bf kf = __builtin_bit_cast(v8bf, *(const v4i*)(rowp + 16 * (S::SWZ ? (lp ^ (kr & 7)) : lp)));
+#pragma unroll
+        for (int ht = 0; ht < kWHt; ++ht) acc[ht][kt] = mfma_bf16_16x16x32(qf[ht][ks], kf, acc[ht][kt]);
       }
     }
   };
 
   // ---- pass 1: lse of every head over keys 0 .. n-1 (base 2)
-  float m[4], l[4];
+  float m[kWHt][4], l[kWHt][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) m[r] = -INFINITY, l[r] = 0.0f;
-  load_chunk<S>(kbuf[0], seq, 0, n, wave, lane);
+  for (int ht = 0; ht < kWHt; ++ht)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[ht][r] = -INFINITY, l[ht][r] = 0.0f;
+  load_chunk<S>(kbuf[0], seq, 0, n_max, wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int st = c & 1;
-    if (c + 1 < nch) load_chunk<S>(kbuf[st ^ 1], seq, kWChunk * (c + 1), n, wave, lane);
-    v4f acc[2];
+    if (c + 1 < nch) load_chunk<S>(kbuf[st ^ 1], seq, kWChunk * (c + 1), n_max, wave, lane);
+    v4f acc[kWHt][2];
     scores(st, acc);
     const bool ok0 = kWChunk * c + li < n, ok1 = kWChunk * c + 16 + li < n;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x0 = ok0 ? acc[0][r] * a.scale_log2 : -INFINITY;
-      const float x1 = ok1 ? acc[1][r] * a.scale_log2 : -INFINITY;
-      const float mn = fmaxf(m[r], fmaxf(x0, x1));
-      const float ms = mn == -INFINITY ? 0.0f : mn;  // nothing seen yet: every term is 0
-      l[r] = l[r] * fast_exp2(m[r] - ms) + fast_exp2(x0 - ms) + fast_exp2(x1 - ms);
-      m[r] = mn;
-    }
+    for (int ht = 0; ht < kWHt; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x0 = ok0 ? acc[ht][0][r] * a.scale_log2 : -INFINITY;
+        const float x1 = ok1 ? acc[ht][1][r] * a.scale_log2 : -INFINITY;
+        const float mn = fmaxf(m[ht][r], fmaxf(x0, x1));
+        const float ms = mn == -INFINITY ? 0.0f : mn;  // nothing seen yet: every term is 0
+        l[ht][r] = l[ht][r] * fast_exp2(m[ht][r] - ms) + fast_exp2(x0 - ms) + fast_exp2(x1 - ms);
+        m[ht][r] = mn;
+      }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  float lse2[4];
+  float lse2[kWHt][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mm = m[r], ll = l[r];
+  for (int ht = 0; ht < kWHt; ++ht)
 #pragma unroll
-    for (int o = 1; o < 16; o <<= 1) {
-      const float mo = xor_lanes(mm, o), lo = xor_lanes(ll, o);
-      const float mn = fmaxf(mm, mo);
-      const float ms = mn == -INFINITY ? 0.0f : mn;
-      ll = ll * fast_exp2(mm - ms) + lo * fast_exp2(mo - ms);
-      mm = mn;
+    for (int r = 0; r < 4; ++r) {
+      float mm = m[ht][r], ll = l[ht][r];
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float mo = xor_lanes(mm, o), lo = xor_lanes(ll, o);
+        const float mn = fmaxf(mm, mo);
+        const float ms = mn == -INFINITY ? 0.0f : mn;
+        ll = ll * fast_exp2(mm - ms) + lo * fast_exp2(mo - ms);
+        mm = mn;
+      }
+      lse2[ht][r] = mm + fast_log2(ll);  // key 0 is always present: finite for every present head
     }
-    lse2[r] = mm + fast_log2(ll);  // key 0 is always present: finite for every head
-  }
 
   // ---- pass 2: target[row, s] = (1/H) sum_h exp2(z * log2e - lse2[h])
-  float* trow = a.target + (size_t)row * a.Lk;
-  load_chunk<S>(kbuf[0], seq, 0, n, wave, lane);
+  load_chunk<S>(kbuf[0], seq, 0, n_max, wave, lane);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int c = 0; c < nch; ++c) {
     const int st = c & 1;
-    if (c + 1 < nch) load_chunk<S>(kbuf[st ^ 1], seq, kWChunk * (c + 1), n, wave, lane);
-    v4f acc[2];
+    if (c + 1 < nch) load_chunk<S>(kbuf[st ^ 1], seq, kWChunk * (c + 1), n_max, wave, lane);
+    v4f acc[kWHt][2];
     scores(st, acc);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       float s = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s += hv[r] ? fast_exp2(fmaf(acc[kt][r], a.scale_log2, -lse2[r])) : 0.0f;
+      for (int ht = 0; ht < kWHt; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s += hv[ht][r] ? fast_exp2(fmaf(acc[ht][kt][r], a.scale_log2, -lse2[ht][r])) : 0.0f;
       s += xor_lanes(s, 16);
       s += xor_lanes(s, 32);
       if (g == 0) red[st][wave][16 * kt + li] = s;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (threadIdx.x < kWChunk) {
-      const int key = kWChunk * c + (int)threadIdx.x;
-      float t = 0.0f;
+    if (threadIdx.x < kWRows * kWChunk) {
+      const int r2 = threadIdx.x / kWChunk, kk = threadIdx.x % kWChunk;
+      const int tt = t0 + r2;
+      const int key = kWChunk * c + kk;
+      if (tt < a.Lq && key < min(a.q_start + tt + 1, a.Lk)) {
+        float v = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWWaves; ++w) t += red[st][w][threadIdx.x];
-      if (key < n) trow[key] = t * a.inv_heads;
+        for (int w = 0; w < WPR; ++w) v += red[st][r2 * WPR + w][kk];
+        a.target[((size_t)bq * a.Lq + tt) * a.Lk + key] = v * a.inv_heads;
+      }
     }
   }
 }
@@ -273,7 +301,7 @@ __global__ __launch_bounds__(kKlThreads) void warmup_kl_kernel(WarmupArgs a) {
 }  // namespace
 
 hipError_t launch_warmup_target(const WarmupArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)((long long)a.B * a.Lq)), block(64 * kWWaves);
+  const dim3 grid((unsigned)((long long)a.B * ((a.Lq + kWRows - 1) / kWRows))), block(64 * kWWaves);
   if (a.Dv == 512 && a.Dr == 64) return launch_kernel((const void*)warmup_target_kernel<576>, grid, block, 0, stream, a);
   if (a.Dv == 64 && a.Dr == 16) return launch_kernel((const void*)warmup_target_kernel<80>, grid, block, 0, stream, a);
   return hipErrorInvalidValue;
