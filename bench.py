@@ -166,7 +166,7 @@ def bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws,
                      "frac": tf / PEAK_BF16_TFLOPS, "kernel": "sparse_mla_attn_bwd", "traffic": None},
         "algorithmic_flop": flop,
         "workspace_bytes": bws_bytes,
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_pass(wl, args.cpu_seconds, "bwd"),
     }
     print(json.dumps(result))
 
@@ -250,7 +250,7 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
         "kernels": kernels,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "kernel": "warmup_target", "traffic": None},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_pass(wl, args.cpu_seconds, "warmup"),
     }
     print(json.dumps(result))
 
@@ -295,6 +295,49 @@ def cpu_baseline(wl, target_s: float):
     return {"value": n / secs, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} query rows evenly spaced over the {wl.q_len}-token sequence "
                       f"(indexer + top-k + attention per row, {secs:.1f} s wall)"}
+
+
+def cpu_baseline_pass(wl, target_s: float, which: str):
+    """The oracle (as it stands) timed on an evenly spaced row sample for the
+    backward ("bwd": dq and dkv of the sampled rows, their indices from the
+    oracle's forward, untimed) or the warm-up step ("warmup": indexer scores,
+    target, KL and the indexer gradients of the sampled rows)."""
+    import numpy as np
+
+    import dsa_inputs
+    import oracle
+
+    k_idx = dsa_inputs.k_idx(wl)
+    kv = dsa_inputs.kv(wl)
+    rng = np.random.default_rng(3)
+
+    def run(n):
+        rows = ((np.arange(n) + 0.5) * (wl.batch * wl.q_len) / n).astype(np.int64)
+        rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+        qi, w, q = dsa_inputs.q_idx(wl, rows), dsa_inputs.w(wl, rows), dsa_inputs.q(wl, rows)
+        if which == "bwd":
+            res = oracle.forward(k_idx, qi, w, q, kv, rb, pos, wl.topk, wl.d_latent, wl.softmax_scale)
+            g = rng.normal(size=(n, wl.heads, wl.d_latent))
+            t0 = time.perf_counter()
+            oracle.sparse_mla_attn_bwd(kv, q, res["indices"], rb, g, wl.d_latent, wl.softmax_scale, wl.batch)
+            return time.perf_counter() - t0
+        t0 = time.perf_counter()
+        scores = oracle.index_scores(k_idx, qi, w, rb, pos)
+        target = oracle.warmup_target(kv, q, rb, pos, wl.softmax_scale)
+        _, d = oracle.warmup_kl(scores, target.astype(np.float32), pos)
+        oracle.index_scores_bwd(k_idx, qi, w, rb, pos, np.nan_to_num(d, nan=0.0))
+        return time.perf_counter() - t0
+
+    threads = oracle.max_threads()
+    pilot_n = max(4, threads)
+    pilot = run(pilot_n)
+    n = int(min(4096, max(pilot_n, pilot_n * target_s / max(pilot, 1e-3))))
+    secs = run(n)
+    what = ("attention backward (dq, dkv) per row" if which == "bwd"
+            else "indexer scores, target, KL and indexer gradients per row")
+    return {"value": n / secs, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows evenly spaced over the {wl.q_len}-token sequence "
+                      f"({what}, {secs:.1f} s wall)"}
 
 
 def main():
