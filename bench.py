@@ -60,6 +60,9 @@ def parse():
                     help="time the attention backward over fixed indices instead of the forward step")
     ap.add_argument("--warmup-objective", action="store_true",
                     help="time the indexer's dense warm-up objective (scores, target, KL) instead")
+    ap.add_argument("--warmup-lse", action="store_true",
+                    help="with --warmup-objective: give the target kernel each head's dense lse "
+                         "(computed once, untimed), as the warm-up's dense attention forward would")
     ap.add_argument("--attn", choices=["sparse", "masked"], default="sparse",
                     help="attention stage: the sparse kernel, or the masked mode for short prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -183,6 +186,11 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
     dq_idx = torch.empty((B, Lq, wl.idx_heads, wl.idx_dim), dtype=torch.float32, device="cuda")
     dw = torch.empty((B, Lq, wl.idx_heads), dtype=torch.float32, device="cuda")
     dk_idx = torch.empty((B, Lk, wl.idx_dim), dtype=torch.float32, device="cuda")
+    lse = None
+    if args.warmup_lse:
+        lse = torch.empty((B, Lq, wl.heads), dtype=torch.float32, device="cuda")
+        dsa.dsa_warmup_target(prob, q, kv, target, lse_out=lse, stream=stream)
+        torch.cuda.synchronize()
 
     def step(ev=None):
         dk_idx.zero_()  # accumulated into by the indexer backward
@@ -191,7 +199,7 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
         dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
         if ev:
             ev[1].record(stream)
-        dsa.dsa_warmup_target(prob, q, kv, target, stream=stream)
+        dsa.dsa_warmup_target(prob, q, kv, target, lse_in=lse, stream=stream)
         if ev:
             ev[2].record(stream)
         dsa.dsa_warmup_kl(prob, scores, target, loss, scores, stream=stream)
@@ -214,7 +222,7 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
     per = {n: [ev[j].elapsed_time(ev[j + 1]) for ev in events] for j, n in enumerate(names)}
     pairs = wl.causal_pairs()
     # algorithmic work: one evaluation of every head's scores per causal pair
-    # (the kernel evaluates them twice: once for the lse, once for the sum)
+    # (without a given lse the kernel evaluates them twice: the lse, then the sum)
     t_flop = 2.0 * wl.heads * wl.d_qk * pairs
     k1_flop = 2.0 * wl.idx_heads * wl.idx_dim * pairs
     kl_bytes = 16.0 * pairs  # scores read twice, target read once, gradient written
@@ -246,7 +254,8 @@ def bench_warmup(args, wl, dsa, prob, q, kv, scores, q_idx, k_idx, w):
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "q_len": Lq, "kv_len": Lk, "heads": wl.heads,
                    "d_latent": wl.d_latent, "d_rope": wl.d_rope, "idx_heads": wl.idx_heads,
-                   "idx_dim": wl.idx_dim, "pass": "dense warm-up step (objective and indexer gradients)"},
+                   "idx_dim": wl.idx_dim, "pass": "dense warm-up step (objective and indexer gradients)",
+                   "attention_lse": "given" if args.warmup_lse else "computed"},
         "kernels": kernels,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "kernel": "warmup_target", "traffic": None},

@@ -222,14 +222,21 @@ int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint1
  *   target[b,t,s] = (1/H) sum_h softmax_s'(softmax_scale * q[b,t,h,:] . kv[b,s',:])[s]
  * for s = 0 .. pos(t) (s < Lk); other entries are left untouched.
  *
- *   q, kv   as for dsa_sparse_mla_attn (topk is not used by this call)
- *   target  [B, Lq, Lk] float32 output
- * Scores are bf16 products with fp32 accumulation; exponentials in fp32.  The
- * kernel computes each head's lse over the row first, so it reads the row's
- * latents twice.  No workspace.
+ *   q, kv    as for dsa_sparse_mla_attn (topk is not used by this call)
+ *   lse_in   [B, Lq, H] float32 or NULL: each head's log-sum-exp (natural
+ *            log) of its dense causal scores, if the caller has it (the
+ *            dense attention forward of the warm-up computes it); the kernel
+ *            then skips its first pass
+ *   lse_out  [B, Lq, H] float32 or NULL: receives that lse when lse_in is
+ *            NULL (giving both is DSA_ERR_SHAPE); entries of absent rows are
+ *            untouched
+ *   target   [B, Lq, Lk] float32 output
+ * Scores are bf16 products with fp32 accumulation; exponentials in fp32.
+ * Without lse_in the kernel computes each head's lse over the row first, so
+ * it reads the row's latents twice.  No workspace.
  */
-int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* kv, float* target,
-                      void* stream);
+int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* kv, const float* lse_in,
+                      float* lse_out, float* target, void* stream);
 
 /*
  * The warm-up's loss and score gradient (same passages): per query row, over

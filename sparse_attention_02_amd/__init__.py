@@ -81,7 +81,7 @@ def _load():
     L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_sparse_mla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp]
+    L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_warmup_kl.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_index_scores_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_masked_mha_attn,
@@ -166,11 +166,12 @@ def dsa_sparse_mla_attn_bwd(problem: Problem, q, kv, indices, out, lse, dout, dq
                                        _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
-def dsa_warmup_target(problem: Problem, q, kv, target, stream=None) -> None:
+def dsa_warmup_target(problem: Problem, q, kv, target, lse_in=None, lse_out=None, stream=None) -> None:
     """The warm-up target: the main attention's distribution summed over the heads
-    and divided by H, dense over s <= pos(t) (include/dsa.h: dsa_warmup_target)."""
-    _check(lib.dsa_warmup_target(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(target),
-                                 _stream(stream)))
+    and divided by H, dense over s <= pos(t); lse_in skips the kernel's lse pass,
+    lse_out receives it (include/dsa.h: dsa_warmup_target)."""
+    _check(lib.dsa_warmup_target(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(lse_in), _ptr(lse_out),
+                                 _ptr(target), _stream(stream)))
 
 
 def dsa_warmup_kl(problem: Problem, scores, target, loss, dscores, stream=None) -> None:

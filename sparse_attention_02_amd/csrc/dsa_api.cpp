@@ -277,15 +277,18 @@ int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint1
                     "sparse_mla_attn_bwd launch");
 }
 
-int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* kv, float* target,
-                      void* stream) {
+int dsa_warmup_target(const dsa_problem* p, const uint16_t* q, const uint16_t* kv, const float* lse_in,
+                      float* lse_out, float* target, void* stream) {
   if (int s = check_common(p)) return s;
   if (int s = check_latent(p)) return s;
   if (int s = check_ptr(q, "q", 16)) return s;
   if (int s = check_ptr(kv, "kv", 16)) return s;
   if (int s = check_ptr(target, "target", 4)) return s;
+  if (lse_in && !aligned(lse_in, 4)) return fail(DSA_ERR_ALIGN, "lse_in is not 4-byte aligned");
+  if (lse_out && !aligned(lse_out, 4)) return fail(DSA_ERR_ALIGN, "lse_out is not 4-byte aligned");
+  if (lse_in && lse_out) return fail(DSA_ERR_SHAPE, "warmup_target: give lse_in or lse_out, not both");
   dsa::WarmupArgs a{};
-  a.q = q; a.kv = kv; a.target = target;
+  a.q = q; a.kv = kv; a.target = target; a.lse_in = lse_in; a.lse_out = lse_out;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start; a.H = p->heads;
   a.Dv = p->d_latent; a.Dr = p->d_rope;
   a.scale_log2 = p->softmax_scale * 1.44269504088896340736f;

@@ -81,6 +81,8 @@ struct WarmupArgs {
   const float* scores;     // [B, Lq, Lk]     indexer scores (KL kernel)
   float* loss;             // [B, Lq]
   float* dscores;          // [B, Lq, Lk]     written for s <= pos(t); may be `scores`
+  const float* lse_in;     // [B, Lq, H]      natural-log lse given by the caller, or null
+  float* lse_out;          // [B, Lq, H]      the computed lse (when lse_in is null), or null
   int B, Lq, Lk, q_start, H, Dv, Dr;
   float scale_log2;        // softmax_scale * log2(e)
   float inv_heads;         // 1 / H

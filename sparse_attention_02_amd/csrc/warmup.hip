@@ -14,7 +14,8 @@
 //  1. target (one block of 8 waves per two adjacent rows, 32 heads per
 //     wave): the rows' causal keys stream through LDS in chunks of 32
 //     contiguous latent rows; S = Q.K^T runs on bf16 MFMA with Q in
-//     registers, so a lane holds 4 heads of one key.  Pass 1 keeps a running max and sum per lane and head
+//     registers, so a lane holds 4 heads of one key.  A caller that has each
+//     head's lse (the dense forward computes it) can pass it and skip pass 1.  Pass 1 keeps a running max and sum per lane and head
 //     and merges them over the 16 key lanes into the head's lse; pass 2
 //     recomputes S and sums exp(z - lse) over the heads (in lane, across the
 //     4 lane rows, then across the waves through LDS) into the target row.
@@ -150,6 +151,16 @@ __global__ __launch_bounds__(64 * kWWaves) void warmup_target_kernel(WarmupArgs 
     }
   };
 
+  float lse2[kWHt][4];
+  if (a.lse_in) {  // block-uniform: the caller has each head's lse (natural log)
+#pragma unroll
+    for (int ht = 0; ht < kWHt; ++ht)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int head = 32 * hg + 16 * ht + 4 * g + r;
+        lse2[ht][r] = hv[ht][r] ? a.lse_in[row * a.H + head] * 1.44269504088896340736f : 0.0f;
+      }
+  } else {
   // ---- pass 1: lse of every head over keys 0 .. n-1 (base 2)
   float m[kWHt][4], l[kWHt][4];
 #pragma unroll
@@ -179,7 +190,6 @@ __global__ __launch_bounds__(64 * kWWaves) void warmup_target_kernel(WarmupArgs 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  float lse2[kWHt][4];
 #pragma unroll
   for (int ht = 0; ht < kWHt; ++ht)
 #pragma unroll
@@ -194,7 +204,10 @@ __global__ __launch_bounds__(64 * kWWaves) void warmup_target_kernel(WarmupArgs 
         mm = mn;
       }
       lse2[ht][r] = mm + fast_log2(ll);  // key 0 is always present: finite for every present head
+      if (a.lse_out && li == 0 && hv[ht][r])
+        a.lse_out[row * a.H + 32 * hg + 16 * ht + 4 * g + r] = lse2[ht][r] * 0.69314718055994530942f;
     }
+  }
 
   // ---- pass 2: target[row, s] = (1/H) sum_h exp2(z * log2e - lse2[h])
   load_chunk<S>(kbuf[0], seq, 0, n_max, wave, lane);

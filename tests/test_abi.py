@@ -166,6 +166,10 @@ def test_warmup_checks():
     s, _ = _status(dsa.dsa_warmup_target, Problem(**{**GOOD.__dict__, "q_start": 1}), FAKE, FAKE, FAKE,
                    stream=0)
     assert s == -2
+    s, _ = _status(dsa.dsa_warmup_target, GOOD, FAKE, FAKE, FAKE, lse_in=FAKE, lse_out=FAKE + 1024, stream=0)
+    assert s == -2
+    s, msg = _status(dsa.dsa_warmup_target, GOOD, FAKE, FAKE, FAKE, lse_in=FAKE + 2, stream=0)
+    assert s == -5 and "lse_in" in msg
     # the KL: only dscores may share a buffer, and only with the scores
     other = FAKE + (1 << 20)
     for args in [(FAKE, FAKE, other, FAKE), (FAKE, other, FAKE, other + 256), (FAKE, other, other + 256, other + 256)]:

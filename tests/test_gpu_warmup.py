@@ -78,6 +78,35 @@ def test_target_prefill4k_sampled_rows(dsa):
     _check_target("prefill4k", got[rows], ref, pos, wl.kv_len)
 
 
+@pytest.mark.parametrize("name", ["tiny", "ragged", "mla_small", "few_queries"])
+def test_target_lse_out_and_lse_in(dsa, name):
+    """lse_out against the oracle's dense lse (its masked mode with every token
+    listed is dense causal attention); a target from lse_in against the oracle
+    and against the two-pass kernel."""
+    wl = _wl(name)
+    inp = Inputs.make(wl)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
+    R = wl.batch * wl.q_len
+    rb, pos = dsa_inputs.row_batch_pos(wl, np.arange(R))
+    q_rows = inp.q.reshape(R, wl.heads, -1)
+    every = np.tile(np.arange(wl.kv_len, dtype=np.int32), (R, 1))
+    _, lse_or = oracle.masked_mha_attn(inp.kv, q_rows, every, rb, pos, wl.d_latent, wl.softmax_scale)
+    t2 = torch.full((wl.batch, wl.q_len, wl.kv_len), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((wl.batch, wl.q_len, wl.heads), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_warmup_target(prob, d["q"], d["kv"], t2, lse_out=lse)
+    t1 = torch.full_like(t2, float("nan"))
+    dsa.dsa_warmup_target(prob, d["q"], d["kv"], t1, lse_in=dev(lse_or.reshape(wl.batch, wl.q_len, wl.heads)))
+    torch.cuda.synchronize()
+    got_lse = lse.reshape(R, wl.heads).cpu().numpy()
+    np.testing.assert_allclose(got_lse, lse_or, rtol=0, atol=2e-5 * max(1.0, float(np.abs(lse_or).max())))
+    ref = oracle.warmup_target(inp.kv, q_rows, rb, pos, wl.softmax_scale)
+    g1 = t1.reshape(R, wl.kv_len).cpu().numpy()
+    _check_target(f"{wl.name} lse_in", g1, ref, pos, wl.kv_len)
+    g2 = t2.reshape(R, wl.kv_len).cpu().numpy()
+    _check_target(f"{wl.name} two-pass", g2, ref, pos, wl.kv_len)
+
+
 def _kl_case(wl):
     """Oracle-made fp32 scores and target for every row of the workload."""
     inp = Inputs.make(wl)
