@@ -29,22 +29,19 @@ namespace dsa {
 
 namespace {
 
-// e4m3fn byte -> bf16 bits (exact): sign | exponent bias 7 -> 127 | 3 mantissa
-// bits; exponent 0 is subnormal (m * 2^-9).  The NaN code is not expected.
-__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 8, e = (c >> 3) & 15u, m = c & 7u;
-  if (e) return s | ((e + 120u) << 7) | (m << 4);
-  return s | (__float_as_uint((float)m * 0x1p-9f) >> 16);
-}
-
-// 8 e4m3 bytes (two words) -> 8 bf16 as 4 packed words
+// 8 e4m3fn bytes (two words) -> 8 bf16 as 4 packed words, exactly: the
+// hardware converts two bytes at a time to fp32 (gfx950's FP8 conversions
+// use the OCP e4m3fn format), and every e4m3 value has at most 4 significant
+// bits, so its bf16 is the upper half of that fp32.
 __device__ __forceinline__ v4i e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   v4i r;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t x = i ? hi : lo;
-    r[2 * i] = (int)(e4m3_to_bf16(x & 0xFFu) | (e4m3_to_bf16((x >> 8) & 0xFFu) << 16));
-    r[2 * i + 1] = (int)(e4m3_to_bf16((x >> 16) & 0xFFu) | (e4m3_to_bf16(x >> 24) << 16));
+    const v2f f0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, false);  // bytes 0, 1
+    const v2f f1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)x, true);   // bytes 2, 3
+    r[2 * i] = (int)((__float_as_uint(f0.x) >> 16) | (__float_as_uint(f0.y) & 0xFFFF0000u));
+    r[2 * i + 1] = (int)((__float_as_uint(f1.x) >> 16) | (__float_as_uint(f1.y) & 0xFFFF0000u));
   }
   return r;
 }
