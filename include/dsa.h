@@ -203,7 +203,8 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
  *              part rounded up to 256 bytes.
  * Requires B*Lq*kp and B*Lk below 2^31 (DSA_ERR_UNSUPPORTED otherwise).
  * The products run on bf16 matrix cores with fp32 accumulation; dout, P, dZ
- * and the partial dkv rows are rounded to bf16.  dq and dkv must not alias
+ * and the partial dkv rows are rounded to bf16 (D = dout . o uses the same
+ * rounded dout as the products, so a row's dZ sums to zero as it should).  dq and dkv must not alias
  * any input.
  */
 int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,

@@ -197,11 +197,18 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
         o0 = *(const v4f*)(orow + d0);
         o1 = *(const v4f*)(orow + d0 + 4);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dpart += g0[e] * o0[e] + g1[e] * o1[e];
       const v4i pk = {(int)pack_bf16x2(g0[0], g0[1]), (int)pack_bf16x2(g0[2], g0[3]),
                       (int)pack_bf16x2(g1[0], g1[1]), (int)pack_bf16x2(g1[2], g1[3])};
       dof[ht][ks] = __builtin_bit_cast(v8bf, pk);
+      // D = dout . o from the same bf16-rounded dout as dP = dout . v, so that
+      // sum_i p_i (dP_i - D) = 0 holds as in exact arithmetic (with fp32 dout
+      // here a one-token row would get dZ ~ rounding of dout instead of 0)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = (uint32_t)pk[w];
+        const float ov0 = w < 2 ? o0[2 * w] : o1[2 * w - 4], ov1 = w < 2 ? o0[2 * w + 1] : o1[2 * w - 3];
+        dpart += __uint_as_float(x << 16) * ov0 + __uint_as_float(x & 0xFFFF0000u) * ov1;
+      }
       // consumed step by step: issuing every step's loads at once would take
       // 256 registers and push the operands above into scratch
       __builtin_amdgcn_sched_barrier(0);

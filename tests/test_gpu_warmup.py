@@ -67,15 +67,24 @@ def test_target_matches_oracle(dsa, name):
     _check_target(wl.name, got, ref, pos, wl.kv_len)
 
 
-def test_target_prefill4k_sampled_rows(dsa):
-    wl = dsa_inputs.WORKLOADS["prefill4k"]
+@pytest.mark.parametrize("name,n_random", [("prefill4k", 10), ("prefill32k", 4)])
+def test_target_full_size_sampled_rows(dsa, name, n_random):
+    """Full-size workloads in the bench's launch configuration, sampled rows."""
+    wl = dsa_inputs.WORKLOADS[name]
     inp = Inputs.make(wl)
-    got = _target_gpu(dsa, wl, inp.device())
-    rows = dsa_inputs.sample_rows(wl, 10)
-    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    d = inp.device()
+    prob = dsa.Problem.from_workload(wl)
     R = wl.batch * wl.q_len
+    t = torch.full((R, wl.kv_len), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_warmup_target(prob, d["q"], d["kv"], t)
+    torch.cuda.synchronize()
+    rows = dsa_inputs.sample_rows(wl, n_random)
+    got = t[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del t, d
+    torch.cuda.empty_cache()
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
     ref = oracle.warmup_target(inp.kv, inp.q.reshape(R, wl.heads, -1)[rows], rb, pos, wl.softmax_scale)
-    _check_target("prefill4k", got[rows], ref, pos, wl.kv_len)
+    _check_target(name, got, ref, pos, wl.kv_len)
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "mla_small", "few_queries"])
@@ -202,13 +211,11 @@ def _index_bwd_case(dsa, wl, rows=None, seed=5):
     R = wl.batch * wl.q_len
     rb_all, pos_all = dsa_inputs.row_batch_pos(wl, np.arange(R))
     rng = np.random.default_rng(seed)
-    g = rng.normal(size=(R, wl.kv_len)).astype(np.float32)
-    g[np.arange(wl.kv_len)[None, :] > pos_all[:, None]] = np.nan  # never read
     sel = np.arange(R) if rows is None else np.asarray(rows)
-    if rows is not None:
-        keep = np.zeros(R, bool)
-        keep[sel] = True
-        g[~keep] = np.where(np.isnan(g[~keep]), np.nan, 0.0)
+    # gradient on the selected rows (0 elsewhere), NaN past pos(t): never read
+    g = np.zeros((R, wl.kv_len), np.float32)
+    g[sel] = rng.normal(size=(sel.size, wl.kv_len))
+    g[sel] = np.where(np.arange(wl.kv_len)[None, :] > pos_all[sel][:, None], np.nan, g[sel])
     dq = torch.full((wl.batch, wl.q_len, wl.idx_heads, wl.idx_dim), float("nan"), dtype=torch.float32, device="cuda")
     dw = torch.full((wl.batch, wl.q_len, wl.idx_heads), float("nan"), dtype=torch.float32, device="cuda")
     dk = torch.zeros((wl.batch, wl.kv_len, wl.idx_dim), dtype=torch.float32, device="cuda")
@@ -218,9 +225,12 @@ def _index_bwd_case(dsa, wl, rows=None, seed=5):
     dq_or, dw_or, dk_or = oracle.index_scores_bwd(inp.k_idx, inp.q_idx.reshape(R, wl.idx_heads, -1)[sel],
                                                   inp.w.reshape(R, -1)[sel], rb, pos,
                                                   np.nan_to_num(g[sel].astype(np.float64), nan=0.0))
-    _ib_check(f"{wl.name} dq_I", dq.reshape(R, wl.idx_heads, -1).cpu().numpy()[sel], dq_or, IB_TOL)
-    _ib_check(f"{wl.name} dw", dw.reshape(R, -1).cpu().numpy()[sel], dw_or, DW_TOL)
+    sel_t = torch.from_numpy(sel).cuda()
+    _ib_check(f"{wl.name} dq_I", dq.reshape(R, wl.idx_heads, -1)[sel_t].cpu().numpy(), dq_or, IB_TOL)
+    _ib_check(f"{wl.name} dw", dw.reshape(R, -1)[sel_t].cpu().numpy(), dw_or, DW_TOL)
     _ib_check(f"{wl.name} dk_I", dk.cpu().numpy(), dk_or, IB_TOL)
+    del dq, dw, dk, d
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "few_queries", "mla_small", "k_above_len", "wide_indexer",
@@ -229,6 +239,7 @@ def test_index_scores_bwd_matches_oracle(dsa, name):
     _index_bwd_case(dsa, _wl(name))
 
 
-def test_index_scores_bwd_prefill4k_sampled_rows(dsa):
-    wl = dsa_inputs.WORKLOADS["prefill4k"]
-    _index_bwd_case(dsa, wl, rows=dsa_inputs.sample_rows(wl, 6))
+@pytest.mark.parametrize("name,n_random", [("prefill4k", 6), ("prefill32k", 4)])
+def test_index_scores_bwd_full_size_sampled_rows(dsa, name, n_random):
+    wl = dsa_inputs.WORKLOADS[name]
+    _index_bwd_case(dsa, wl, rows=dsa_inputs.sample_rows(wl, n_random))
