@@ -298,8 +298,11 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
         a.ws_dzk[o] = (uint16_t)(pack_bf16x2(zv[e] * a.scale, 0.0f) & 0xFFFFu);
       }
     }
-    // the next chunk's copies are complete and every wave is done with this one
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the next chunk's copies are complete and every wave is done with this
+    // one.  Vector memory operations retire in issue order, so waiting until
+    // only this chunk's stores (1 + 16 per head tile, issued after the copies)
+    // may be outstanding is enough: the stores drain behind the next chunk.
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(17 * S::HTQ) : "memory");
     __syncthreads();
   }
 }
@@ -649,8 +652,11 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_part_kernel(AttnBwdArgs 
         *(v2i*)(prow + 16 * (wave + NW * j) + 4 * g) = (v2i){(int)pack_bf16x2(acc[j][kt][0], acc[j][kt][1]),
                                                              (int)pack_bf16x2(acc[j][kt][2], acc[j][kt][3])};
     }
-    // the next chunk's copies are complete and every wave is done with this one
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the next chunk's copies are complete and every wave is done with this
+    // one; only this chunk's 2 * TPW partial-row stores (issued after the
+    // copies; vector memory operations retire in issue order) may still be
+    // outstanding
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * TPW) : "memory");
     __syncthreads();
   }
 }
