@@ -81,11 +81,19 @@ def source_hash(rel: str) -> str:
 
 
 def algorithmic(wl):
-    """Algorithmic work per launch (only what the method must do)."""
+    """Algorithmic work per launch (only what the method must do).  `bytes`
+    counts every latent row a query gathers; `hbm_min_bytes` is the least HBM
+    traffic the kernel needs: each byte of its inputs and outputs once, the
+    gather counted at most once per cached latent row (a gather that fits the
+    caches costs the cache once; a larger one, e.g. decode over many
+    sequences, costs what it gathers)."""
     causal = wl.causal_pairs()
     sel = wl.selected_pairs()
     rows = wl.batch * wl.q_len
-    return {
+    attn_io = rows * wl.heads * (2 * wl.d_qk + 4 * wl.d_latent + 4) + 4.0 * rows * wl.topk
+    gathered = 2.0 * wl.d_qk * sel
+    cache = 2.0 * wl.d_qk * wl.batch * wl.kv_len
+    work = {
         "index_scores": dict(
             flop=2.0 * wl.idx_heads * wl.idx_dim * causal,
             bytes=rows * wl.idx_heads * (wl.idx_dim + 4) + wl.batch * wl.kv_len * wl.idx_dim
@@ -103,6 +111,44 @@ def algorithmic(wl):
             bytes=rows * wl.heads * (2 * wl.d_qk + 4 * wl.d_latent + 4) + 4.0 * rows * wl.topk
             + 2.0 * wl.d_qk * causal),
     }
+    for name, w in work.items():
+        w["hbm_min_bytes"] = w["bytes"]
+    work["sparse_mla_attn"]["hbm_min_bytes"] = attn_io + min(gathered, cache)
+    work["masked_mha_attn"]["hbm_min_bytes"] = attn_io + min(2.0 * wl.d_qk * causal, cache)
+    return work
+
+
+KERNEL_PEAK_TFLOPS = {"index_scores": PEAK_FP8_TFLOPS, "sparse_mla_attn": PEAK_BF16_TFLOPS,
+                      "masked_mha_attn": PEAK_BF16_TFLOPS, "topk": None}
+
+
+def roofline_ms(name, w):
+    """The kernel's time at its roofline: the larger of its work at the MFMA peak
+    of its dtype and its least HBM traffic at the HBM peak."""
+    t_mem = w["hbm_min_bytes"] / (PEAK_HBM_GBS * 1e9) * 1e3
+    peak = KERNEL_PEAK_TFLOPS[name]
+    t_mfma = w["flop"] / (peak * 1e12) * 1e3 if peak and w["flop"] else 0.0
+    return max(t_mem, t_mfma)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def metric_name(wl) -> str:
+    if wl.name == "prefill32k":
+        return "DSA query tokens/s at L=32K prefill"
+    if wl.q_len == 1:
+        return f"DSA query tokens/s, {wl.name} ({wl.batch} sequences x 1 query over {wl.kv_len} tokens)"
+    return f"DSA query tokens/s, {wl.name} ({wl.batch} x {wl.q_len} queries, positions {wl.q_start}.." \
+           f"{wl.q_start + wl.q_len - 1} of {wl.kv_len})"
 
 
 def bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws, ws_bytes, aws, aws_bytes,
@@ -114,7 +160,7 @@ def bench_bwd(args, wl, dsa, prob, to_dev, q, kv, scores, indices, out, lse, ws,
     stream = torch.cuda.current_stream()
     dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
     dsa.dsa_topk(prob, scores, indices, ws, ws_bytes, stream=stream)
-    dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
+    dsa.dsa_sparse_mla_attn_ws(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
     torch.cuda.synchronize()
     del scores
     torch.cuda.empty_cache()
@@ -302,7 +348,8 @@ def cpu_baseline(wl, target_s: float):
     n = int(min(4096, max(pilot_n, pilot_n * target_s / max(pilot, 1e-3))))
     secs = run(n)
     return {"value": n / secs, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} query rows evenly spaced over the {wl.q_len}-token sequence "
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{n} query rows evenly spaced over the {wl.batch * wl.q_len} query rows "
                       f"(indexer + top-k + attention per row, {secs:.1f} s wall)"}
 
 
@@ -345,7 +392,8 @@ def cpu_baseline_pass(wl, target_s: float, which: str):
     what = ("attention backward (dq, dkv) per row" if which == "bwd"
             else "indexer scores, target, KL and indexer gradients per row")
     return {"value": n / secs, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} query rows evenly spaced over the {wl.q_len}-token sequence "
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "sample": f"{n} query rows evenly spaced over the {wl.batch * wl.q_len} query rows "
                       f"({what}, {secs:.1f} s wall)"}
 
 
@@ -414,7 +462,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         if args.attn == "sparse":
-            dsa.dsa_sparse_mla_attn(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
+            dsa.dsa_sparse_mla_attn_ws(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
         else:
             dsa.dsa_masked_mha_attn(prob, q, kv, indices, out, lse, stream=stream)
         if ev is not None:
@@ -456,6 +504,7 @@ def main():
         avg_ms = float(np.mean(per[n]))
         k = {"avg_ms": avg_ms, "median_ms": float(np.median(per[n])), "min_ms": float(np.min(per[n])),
              "algorithmic_flop": work[n]["flop"], "algorithmic_bytes": work[n]["bytes"],
+             "hbm_min_bytes": work[n]["hbm_min_bytes"], "roofline_ms": roofline_ms(n, work[n]),
              "hbm_bytes_per_launch": traffic_for(n)}
         if work[n]["flop"]:
             tf = work[n]["flop"] / (avg_ms * 1e-3) / 1e12
@@ -477,8 +526,9 @@ def main():
     roof["traffic"] = kd["hbm_bytes_per_launch"]
 
     value = wl.batch * wl.q_len * args.steps / wall
+    ceiling_ms = sum(kernels[n]["roofline_ms"] for n in names)
     result = {
-        "metric": "DSA query tokens/s at L=32K prefill",
+        "metric": metric_name(wl),
         "value": value,
         "unit": "query tokens/s",
         "n_gpus": 1,
@@ -497,6 +547,9 @@ def main():
                    "idx_dim": wl.idx_dim, "heads": wl.heads, "d_latent": wl.d_latent,
                    "d_rope": wl.d_rope, "attn": args.attn},
         "roofline": roof,
+        # the whole step against the sum of its kernels' roofline times
+        "end_to_end": {"ceiling_ms": ceiling_ms, "ms_per_step": ms_per_step, "frac": ceiling_ms / ms_per_step,
+                       "ceiling_query_tokens_per_s": wl.batch * wl.q_len / (ceiling_ms * 1e-3)},
         "indexer_fp8_tflops": kernels["index_scores"]["tflops"],
         "indexer_frac_of_fp8_peak": kernels["index_scores"]["frac_of_mfma_peak"],
         "kernels": kernels,

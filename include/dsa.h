@@ -18,6 +18,8 @@
  *                        head, one selection per query position (lightning
  *                        indexer post, same section; spec sheet, "Inference
  *                        efficiency" table, KV-cache design).
+ *   dsa_sparse_mla_attn_ws  the same with a workspace that lets few rows
+ *                        (decode) spread over the whole chip.
  *   dsa_sparse_mla_attn_bwd  gradients of the sparse attention (dq, dkv) over
  *                        fixed indices, for the sparse training stage.
  *   dsa_warmup_target    the main attention's distribution summed over the
@@ -112,7 +114,10 @@ enum dsa_op {
  * The dot products run on FP8 matrix cores with fp32 accumulation; the ReLU
  * and the weighted head sum in fp32.  Zero results are +0.  When every partial
  * sum is exactly representable in fp32 (true for the 0.25-step value grids of
- * [-4,4] for q/k and [-1,1] for w) the result equals the exact value.
+ * [-4,4] for q/k and [-1,1] for w) the result equals the exact value; for
+ * other finite inputs it is the exact value within fp32 accumulation error.
+ * Every finite e4m3fn code (subnormals and +-448 included) is read as its OCP
+ * value; the NaN codes 0x7F and 0xFF give unspecified scores.
  */
 int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx,
                      const float* w, float* scores, void* stream);
@@ -151,6 +156,9 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
  *   lse[b,t,h]   = log(sum_s exp(z_s))             (natural log)
  * The value of a latent is its first D_v columns; the last D_r columns (rope)
  * only enter the scores.  A row with no valid entry gives out = 0, lse = -inf.
+ * ("DeepSeek V3.2 and the lightning indexer", "How the lightning indexer
+ * works": the main attention runs only over the selected tokens, MLA in its
+ * MQA mode with one latent per token shared by all heads.)
  *
  *   q       [B, Lq, H, D_qk] bfloat16 (raw bits)
  *   kv      [B, Lk, D_qk]    bfloat16 latent cache, one row per token shared
@@ -158,19 +166,30 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
  *   indices [B, Lq, k]       int32
  *   out     [B, Lq, H, D_v]  float32 output
  *   lse     [B, Lq, H]       float32 output, or NULL
- *   workspace: optional device scratch, 16-byte aligned.  When it holds at
- *              least dsa_workspace_size(p, DSA_OP_SPARSE_MLA_ATTN) bytes and
- *              that size is non-zero (fewer query rows than compute units),
- *              each row's selected entries are split over several blocks whose
- *              normalised partial results (and their lse) are merged by a second
- *              kernel; otherwise (NULL, or too small) one block handles a row.
- *              Results agree within rounding either way.
- * Scores and the softmax run in fp32; the probabilities are rounded to bf16
- * for the value product on bf16 matrix cores with fp32 accumulation.
+ * One block handles a query row.  Scores and the softmax run in fp32; the
+ * probabilities are rounded to bf16 for the value product on bf16 matrix
+ * cores with fp32 accumulation.  No workspace.
  */
 int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
-                        const int32_t* indices, float* out, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const int32_t* indices, float* out, float* lse, void* stream);
+
+/*
+ * dsa_sparse_mla_attn with a workspace that lets it split rows: the same
+ * arguments and results, plus
+ *   workspace: device scratch, 16-byte aligned, or NULL.  When it holds at
+ *              least dsa_workspace_size(p, DSA_OP_SPARSE_MLA_ATTN) bytes and
+ *              that size is non-zero (fewer query rows than compute units, as
+ *              in decode), each row's selected entries are split over several
+ *              blocks whose normalised partial results (and their lse) are
+ *              merged by a second kernel; otherwise (NULL, too small, or a size
+ *              of 0) it runs exactly as dsa_sparse_mla_attn.  The split keeps
+ *              rows x parts x H x (D_v + 1) floats there; contents on return
+ *              are unspecified.  Results agree with the unsplit call within
+ *              rounding.
+ */
+int dsa_sparse_mla_attn_ws(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                           const int32_t* indices, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * Backward of dsa_sparse_mla_attn over fixed indices: the gradients the sparse
@@ -302,13 +321,17 @@ int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
                         const int32_t* indices, float* out, float* lse, void* stream);
 
 /*
- * dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream.
+ * dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn on one stream: the
+ * whole sparse attention of a layer, in the order the lightning-indexer post
+ * gives it ("How the lightning indexer works": score every preceding token,
+ * keep the top k per query, attend over those only).
  * The scores live in the workspace (at least dsa_workspace_size(p,
  * DSA_OP_FORWARD) bytes, 256-byte aligned).  `indices` may be NULL; when given
  * ([B, Lq, k] int32) it receives the selection, otherwise the selection is
  * kept in the workspace, together with the top-k and attention scratch.
- * Results are bit-identical to the three separate calls made with workspaces
- * of the sizes dsa_workspace_size() reports for them.
+ * Results are bit-identical to dsa_index_scores, dsa_topk and
+ * dsa_sparse_mla_attn_ws called with workspaces of the sizes
+ * dsa_workspace_size() reports for them.
  */
 int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
                 const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,

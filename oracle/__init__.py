@@ -118,6 +118,81 @@ def index_scores(k_idx, q_idx_rows, w_rows, row_batch, row_pos, fill=np.nan) -> 
     return out
 
 
+def on_score_grid(q_idx, k_idx, w) -> bool:
+    """True when every decoded q_I / k_I value is a multiple of 1/4 with
+    magnitude <= 4 and every weight a multiple of 1/4 with magnitude <= 1 (the
+    value grids of the synthetic workloads)."""
+    table = e4m3_to_float64(np.arange(256))
+    ok_code = np.zeros(256, dtype=bool)
+    fin = np.isfinite(table)
+    ok_code[fin] = (np.abs(table[fin]) <= 4.0) & (table[fin] * 4 == np.round(table[fin] * 4))
+    if not ok_code[np.asarray(q_idx, dtype=np.uint8)].all():
+        return False
+    if not ok_code[np.asarray(k_idx, dtype=np.uint8)].all():
+        return False
+    w = np.asarray(w, dtype=np.float64)
+    return bool(((np.abs(w) <= 1.0) & (w * 4 == np.round(w * 4))).all())
+
+
+def index_scores_blas(k_idx, q_idx_rows, w_rows, row_batch, row_pos, fill=np.nan,
+                      rows_per_block: int = 32) -> np.ndarray:
+    """The same lightning-indexer definition as index_scores, evaluated with
+    library matrix products in double precision, for checking whole outputs of
+    large workloads (arguments and result as for index_scores).
+
+    Steps, in the definition's order ("DeepSeek V3.2 and the lightning
+    indexer", "How the lightning indexer works"): decode the FP8 codes; the
+    per-head dot products D[r,j,s] = q_I[r,j,:] . k_I[b_r,s,:] as one matrix
+    product; the ReLU; the weighted head sum I[r,s] = sum_j w[r,j] ReLU(D[r,j,s])
+    as a batched product; +0 for -0; one rounding to fp32.
+
+    Exactness (why the library's summation order cannot matter): it accepts
+    only inputs on the workloads' grids (on_score_grid), and needs
+    H_I * d_I <= 8192.  Then every product q*k is a multiple of 2^-4 below 2^4
+    in magnitude, every partial sum of a dot product a multiple of 2^-4 below
+    2^11, every term w * ReLU(D) a multiple of 2^-6, and every partial sum of
+    the head sum a multiple of 2^-6 below 2^17 in magnitude: at most 24
+    significant bits, so each double-precision sum and the final fp32 rounding
+    are exact, and the result equals index_scores bit for bit.  Other inputs
+    raise ValueError.  Rows are processed a block at a time only to bound
+    memory; each row's value is its own definition.
+    """
+    import torch
+
+    k_idx = np.ascontiguousarray(k_idx, dtype=np.uint8)
+    B, Lk, dI = k_idx.shape
+    q_idx_rows = np.ascontiguousarray(q_idx_rows, dtype=np.uint8)
+    R, HI, dI2 = q_idx_rows.shape
+    assert dI2 == dI
+    w_rows = np.ascontiguousarray(w_rows, dtype=np.float32)
+    assert w_rows.shape == (R, HI)
+    rb = np.asarray(row_batch, dtype=np.int64)
+    rp = np.asarray(row_pos, dtype=np.int64)
+    assert rb.shape == (R,) and rp.shape == (R,)
+    assert (rb >= 0).all() and (rb < B).all() and (rp >= 0).all()
+    if HI * dI > 8192 or not on_score_grid(q_idx_rows, k_idx, w_rows):
+        raise ValueError("index_scores_blas is exact only on the 0.25-step grids with H_I * d_I <= 8192")
+    table = torch.from_numpy(e4m3_to_float64(np.arange(256)))
+    out = np.full((R, Lk), fill, dtype=np.float32)
+    for b in np.unique(rb):
+        keys = table[torch.from_numpy(k_idx[b].astype(np.int64))]                 # [Lk, dI]
+        rows = np.nonzero(rb == b)[0]
+        rows = rows[np.argsort(rp[rows], kind="stable")]
+        for i0 in range(0, len(rows), rows_per_block):
+            blk = rows[i0:i0 + rows_per_block]
+            n = int(min(rp[blk].max() + 1, Lk))
+            q = table[torch.from_numpy(q_idx_rows[blk].astype(np.int64))]         # [r, HI, dI]
+            d = torch.from_numpy(q.reshape(-1, dI).numpy() @ keys[:n].numpy().T)  # [r*HI, n]
+            d.clamp_(min=0.0)                                                      # ReLU
+            wt = torch.from_numpy(w_rows[blk].astype(np.float64))[:, None, :]      # [r, 1, HI]
+            score = torch.bmm(wt, d.view(len(blk), HI, n))[:, 0, :] + 0.0         # [r, n], -0 -> +0
+            score = score.to(torch.float32).numpy()
+            for j, r in enumerate(blk):
+                m = int(min(rp[r] + 1, Lk))
+                out[r, :m] = score[j, :m]
+    return out
+
+
 def topk(scores_rows, row_pos, k: int) -> np.ndarray:
     """Top-k selection per row over candidates s <= pos_r.
 

@@ -77,14 +77,16 @@ def _load():
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     L.dsa_index_scores.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
-    L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.dsa_sparse_mla_attn_ws.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_sparse_mla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_warmup_kl.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_index_scores_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_masked_mha_attn,
+    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_sparse_mla_attn_ws,
+              L.dsa_masked_mha_attn,
               L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_warmup_target, L.dsa_warmup_kl,
               L.dsa_index_scores_bwd):
         f.restype = i32
@@ -144,15 +146,23 @@ def dsa_topk(problem: Problem, scores, indices, workspace=None, workspace_bytes:
                         workspace_bytes, _stream(stream)))
 
 
-def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, workspace=None,
-                        workspace_bytes: int = 0, stream=None) -> None:
-    """Sparse MQA-mode attention over the selected latents (include/dsa.h: dsa_sparse_mla_attn).
-    The workspace is optional (see dsa_workspace_size(problem, DSA_OP_SPARSE_MLA_ATTN))."""
+def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:
+    """Sparse MQA-mode attention over the selected latents, one block per row
+    (include/dsa.h: dsa_sparse_mla_attn)."""
+    _check(lib.dsa_sparse_mla_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
+                                   _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def dsa_sparse_mla_attn_ws(problem: Problem, q, kv, indices, out, lse=None, workspace=None,
+                           workspace_bytes: int = 0, stream=None) -> None:
+    """The same with a workspace that lets few rows split over several blocks
+    (include/dsa.h: dsa_sparse_mla_attn_ws; size from
+    dsa_workspace_size(problem, DSA_OP_SPARSE_MLA_ATTN))."""
     if workspace is not None and not isinstance(workspace, int) and workspace_bytes == 0:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(lib.dsa_sparse_mla_attn(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
-                                   _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
-                                   _stream(stream)))
+    _check(lib.dsa_sparse_mla_attn_ws(ctypes.byref(problem.c()), _ptr(q), _ptr(kv), _ptr(indices),
+                                      _ptr(out), _ptr(lse), _ptr(workspace), workspace_bytes,
+                                      _stream(stream)))
 
 
 def dsa_sparse_mla_attn_bwd(problem: Problem, q, kv, indices, out, lse, dout, dq, dkv,

@@ -229,9 +229,9 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
                     "topk launch");
 }
 
-int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
-                        const int32_t* indices, float* out, float* lse, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+int dsa_sparse_mla_attn_ws(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                           const int32_t* indices, float* out, float* lse, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   if (int s = check_common(p)) return s;
   if (int s = check_attn(p)) return s;
   if (int s = check_ptr(q, "q", 16)) return s;
@@ -244,6 +244,11 @@ int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
                         attn_args(p, q, kv, indices, out, lse, workspace, workspace_bytes),
                         (hipStream_t)stream),
                     "sparse_mla_attn launch");
+}
+
+int dsa_sparse_mla_attn(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,
+                        const int32_t* indices, float* out, float* lse, void* stream) {
+  return dsa_sparse_mla_attn_ws(p, q, kv, indices, out, lse, nullptr, 0, stream);
 }
 
 int dsa_sparse_mla_attn_bwd(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,

@@ -57,7 +57,7 @@ def run_stages(prob, d, wl, fill_scores=float("-inf"), lse=True):
     dsa.dsa_topk(prob, scores, indices, ws, ws_bytes)
     aws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
     aws = torch.empty(aws_bytes, dtype=torch.uint8, device="cuda") if aws_bytes else None
-    dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], indices, out, lse_t, aws, aws_bytes)
+    dsa.dsa_sparse_mla_attn_ws(prob, d["q"], d["kv"], indices, out, lse_t, aws, aws_bytes)
     torch.cuda.synchronize()
     return scores, indices, out, lse_t
 
@@ -102,34 +102,51 @@ def check_rows(inp: Inputs, rows, scores, indices, out, lse, atol=1e-2, label=""
 
 def check_selection_properties(wl, scores, indices):
     """Properties of the GPU selection that hold at any size, checked on every row:
-    ascending valid prefix, count = min(pos+1, k), values <= pos, -1 padding, and
-    min(selected scores) >= max(unselected candidate scores).
-    `scores` must have been pre-filled with -inf so entries past pos are -inf."""
+    ascending valid prefix, count = min(pos+1, k), values <= pos, -1 padding,
+    min(selected scores) >= max(unselected candidate scores), and the tie rule:
+    among the candidates whose score equals the row's smallest selected score,
+    every selected index is below every unselected one.
+    Entries of `scores` past pos are not read.  Returns the number of rows
+    where the tie rule binds (an unselected candidate ties the threshold)."""
     B, Lq, Lk, k = wl.batch, wl.q_len, wl.kv_len, wl.topk
-    pos = torch.arange(Lq, device="cuda", dtype=torch.int64) + wl.q_start
+    dev = scores.device
+    pos = torch.arange(Lq, device=dev, dtype=torch.int64) + wl.q_start
     n_exp = torch.clamp(torch.clamp(pos + 1, max=Lk), max=k)              # [Lq]
     idx = indices.to(torch.int64)                                          # [B, Lq, k]
     valid = idx >= 0
     assert torch.equal(valid.sum(-1), n_exp.expand(B, Lq)), "selected count != min(pos+1, k)"
-    slot = torch.arange(k, device="cuda")
+    slot = torch.arange(k, device=dev)
     assert torch.equal(valid, (slot[None, None, :] < n_exp[None, :, None]).expand(B, Lq, k)), \
         "padding is not a -1 suffix"
     assert bool(((idx <= pos[None, :, None]) | ~valid).all()), "selected index beyond pos"
     d = idx[..., 1:] - idx[..., :-1]
     assert bool(((d > 0) | ~valid[..., 1:]).all()), "indices not strictly ascending"
-    # threshold property, processed in row blocks to bound memory
-    rows_per = max(1, (1 << 28) // (Lk * 4))
+    # threshold and tie properties, processed in row blocks to bound memory
+    rows_per = max(1, (1 << 27) // (Lk * 4))
+    col = torch.arange(Lk, device=dev, dtype=torch.int64)
+    big = torch.iinfo(torch.int64).max
+    n_tied_rows = 0
     for b in range(B):
         for t0 in range(0, Lq, rows_per):
             t1 = min(Lq, t0 + rows_per)
-            s = scores[b, t0:t1].clone()
+            s = scores[b, t0:t1]
             ii = idx[b, t0:t1]
             vv = valid[b, t0:t1]
             safe = torch.where(vv, ii, torch.zeros_like(ii))
             sel = torch.gather(s, 1, safe)
             sel = torch.where(vv, sel, torch.full_like(sel, float("inf")))
             min_sel = sel.min(1).values
-            s.scatter_(1, safe, float("-inf"))
-            max_rest = s.max(1).values
-            ok = (min_sel >= max_rest)
-            assert bool(ok.all()), f"threshold property fails in batch {b} rows {t0}..{t1}"
+            # -1 slots point at column 0 with a zero count, so they mark nothing
+            chosen = torch.zeros(s.shape, dtype=torch.int32, device=dev)
+            chosen.scatter_add_(1, safe, vv.to(torch.int32))
+            chosen = chosen > 0
+            cand = col[None, :] <= pos[t0:t1, None]
+            rest = torch.where(chosen | ~cand, torch.full_like(s, float("-inf")), s)
+            max_rest = rest.max(1).values
+            assert bool((min_sel >= max_rest).all()), f"threshold property fails in batch {b} rows {t0}..{t1}"
+            tied = cand & (s == min_sel[:, None])
+            hi_sel = torch.where(tied & chosen, col[None, :], torch.full_like(col, -1)[None, :]).max(1).values
+            lo_rest = torch.where(tied & ~chosen, col[None, :], torch.full_like(col, big)[None, :]).min(1).values
+            assert bool((hi_sel < lo_rest).all()), f"tie rule fails in batch {b} rows {t0}..{t1}"
+            n_tied_rows += int((lo_rest < big).sum())
+    return n_tied_rows

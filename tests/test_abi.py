@@ -29,11 +29,56 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_masked_mha_attn",
+    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_sparse_mla_attn_ws", "dsa_masked_mha_attn",
             "dsa_sparse_mla_attn_bwd", "dsa_forward", "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
     lib = ctypes.CDLL(dsa.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
+
+
+def _declarations():
+    """Return type and parameter types of every function declared in dsa.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    decls = {}
+    for m in re.finditer(r"([A-Za-z_][\w\s\*]*?)\b(dsa_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+        ret = " ".join(m.group(1).split())
+        params = []
+        for a in m.group(3).split(","):
+            a = " ".join(a.replace("*", " * ").split())
+            if a == "void":
+                continue
+            toks = a.split(" ")
+            if toks[-1] not in ("*",) and len(toks) > 1 and toks[-1] not in ("int", "size_t"):
+                toks = toks[:-1]  # drop the parameter name
+            params.append(" ".join(toks).replace(" *", "*"))
+        decls[m.group(2)] = (ret.replace(" *", "*"), params)
+    return decls
+
+
+def test_boundary_signatures():
+    """The calls of the contract keep its exact argument lists, so a caller
+    written to it passes its stream in the stream slot (the split attention
+    takes its workspace through a call of its own)."""
+    d = _declarations()
+    P = "const dsa_problem*"
+    expect = {
+        "dsa_index_scores": ("int", [P, "const uint8_t*", "const uint8_t*", "const float*", "float*", "void*"]),
+        "dsa_topk": ("int", [P, "const float*", "int32_t*", "void*", "size_t", "void*"]),
+        "dsa_sparse_mla_attn": ("int", [P, "const uint16_t*", "const uint16_t*", "const int32_t*", "float*",
+                                        "float*", "void*"]),
+        "dsa_sparse_mla_attn_ws": ("int", [P, "const uint16_t*", "const uint16_t*", "const int32_t*",
+                                           "float*", "float*", "void*", "size_t", "void*"]),
+        "dsa_forward": ("int", [P, "const uint8_t*", "const uint8_t*", "const float*", "const uint16_t*",
+                                "const uint16_t*", "float*", "float*", "int32_t*", "void*", "size_t", "void*"]),
+        "dsa_workspace_size": ("size_t", [P, "int"]),
+        "dsa_status_string": ("const char*", ["int"]),
+        "dsa_last_error": ("const char*", []),
+    }
+    for name, sig in expect.items():
+        assert d.get(name) == sig, f"{name}: declared {d.get(name)}, contract {sig}"
+    # through the binding: the seventh argument of dsa_sparse_mla_attn is the stream
+    assert len(dsa.lib.dsa_sparse_mla_attn.argtypes) == 7
+    assert len(dsa.lib.dsa_sparse_mla_attn_ws.argtypes) == 9
 
 
 def test_status_strings():
@@ -90,6 +135,11 @@ def test_null_and_alignment():
     assert s == -5 and "q_idx" in msg
     s, msg = _status(dsa.dsa_sparse_mla_attn, GOOD, FAKE, FAKE + 2, FAKE, FAKE, stream=0)
     assert s == -5 and "kv" in msg
+    s, msg = _status(dsa.dsa_sparse_mla_attn_ws, GOOD, FAKE, FAKE, FAKE, FAKE, None, FAKE + 8, 1 << 20,
+                     stream=0)
+    assert s == -5 and "workspace" in msg
+    s, msg = _status(dsa.dsa_sparse_mla_attn_ws, GOOD, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 20, stream=0)
+    assert s == -1 and "indices" in msg
     # a null problem pointer
     lib = dsa.lib
     assert lib.dsa_index_scores(None, FAKE, FAKE, FAKE, FAKE, None) == -1

@@ -198,9 +198,14 @@ DW_TOL = 1e-5  # dw: fp32 sums of exact ReLU(u) times fp32 dscores
 
 
 def _ib_check(label, got, ref, tol):
-    err = float(np.abs(got - ref).max())
+    e = np.abs(got - ref)
+    err = float(e.max())
     scale = float(np.abs(ref).max())
-    log(f"[{label}] max-abs {err:.3e} of max|ref| {scale:.3e} (relative {err / max(scale, 1e-30):.2e})")
+    rowmax = np.abs(ref).max(axis=-1)
+    live = rowmax > 0
+    per_row = e.max(axis=-1)[live] / rowmax[live] if live.any() else np.zeros(1)
+    log(f"[{label}] max-abs {err:.3e} of max|ref| {scale:.3e} (relative {err / max(scale, 1e-30):.2e}); "
+        f"per-row relative max {per_row.max():.2e}, p99.9 {np.quantile(per_row, 0.999):.2e}, rows {per_row.size}")
     assert err <= tol * scale + 1e-7, f"{label}: {err} > {tol} * {scale}"
 
 

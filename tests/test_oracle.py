@@ -645,3 +645,58 @@ def test_workload_pair_counts_closed_form():
     assert c["chunked1m"].causal_pairs() == sum(range(2 ** 20 - 4096 + 1, 2 ** 20 + 1))
     assert c["chunked1m"].selected_pairs() == 4096 * 2048
     assert c["prefill2k"].selected_pairs() == c["prefill2k"].causal_pairs() == 2048 * 2049 // 2
+
+
+# ---------------------------------------------------------------------------
+# The matrix-product evaluation of the indexer (for whole outputs at size)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("prefill4k", [0, 1, 2047, 2048, 3001, 4095]),
+                                       ("chunked", [0, 4000, 8191])])
+def test_indexer_blas_equals_the_c_definition_bit_for_bit(name, rows):
+    """index_scores_blas evaluates the same definition with library products;
+    on the workload grids it must equal the C oracle bit for bit, including
+    the NaN fill past pos(t) and +0 for zero scores."""
+    import torch  # noqa: F401  (the evaluation uses torch's CPU kernels)
+    wl = dsa_inputs.WORKLOADS[name]
+    rows = np.arange(wl.batch * wl.q_len) if rows is None else np.asarray(rows)
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    k_idx = dsa_inputs.k_idx(wl)
+    qi, w = dsa_inputs.q_idx(wl, rows), dsa_inputs.w(wl, rows)
+    a = oracle.index_scores(k_idx, qi, w, rb, pos)
+    b = oracle.index_scores_blas(k_idx, qi, w, rb, pos, rows_per_block=3)
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert (b.view(np.uint32) != 0x80000000).all()
+
+
+def test_indexer_blas_extremes_ragged_heads_and_batches():
+    """The largest magnitudes the grid allows (|I| = 2^17: every value +-4, every
+    weight +-1), a ragged head count and width, two sequences with rows in
+    shuffled order, and w < 0 against zero dot products (-0 terms)."""
+    rng = RNG(5)
+    B, Lk, HI, dI, R = 2, 70, 5, 96, 9
+    k = grid(rng, (B, Lk, dI))
+    k[0, :10] = 4.0
+    k[1, 5] = 0.0
+    q = grid(rng, (R, HI, dI))
+    q[0] = 4.0
+    w = grid(rng, (R, HI), -1, 1)
+    w[0] = 1.0
+    w[1] = -1.0
+    rb = np.array([0, 1, 1, 0, 1, 0, 0, 1, 0], np.int32)
+    pos = np.array([9, 69, 5, 0, 33, 69, 12, 40, 2], np.int32)
+    a = oracle.index_scores(enc_e4m3(k), enc_e4m3(q), w.astype(np.float32), rb, pos)
+    b = oracle.index_scores_blas(enc_e4m3(k), enc_e4m3(q), w.astype(np.float32), rb, pos)
+    np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert a[0, 0] == 5 * 96 * 16.0  # five heads of 96 products of 4 * 4, weights 1
+
+
+def test_indexer_blas_refuses_inputs_off_the_grid():
+    rng = RNG(6)
+    k = grid(rng, (1, 20, 32))
+    q = grid(rng, (2, 4, 32))
+    w = grid(rng, (2, 4), -1, 1).astype(np.float32)
+    rb, pos = np.zeros(2, np.int32), np.array([10, 19], np.int32)
+    for kk, qq, ww in [(k * 1.5, q, w), (k, q + 0.125, w), (k, q, w * 0.5 + 0.125), (k * 2, q, w)]:
+        with pytest.raises(ValueError):
+            oracle.index_scores_blas(enc_e4m3(kk), enc_e4m3(qq), ww.astype(np.float32), rb, pos)
