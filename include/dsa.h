@@ -337,6 +337,24 @@ int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx
                 const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * dsa_forward without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops such as decode,
+ * harnesses that forbid allocation).  Same arguments and results as
+ * dsa_forward minus the workspace: the scores, the selection (when `indices`
+ * is NULL) and the top-k and attention scratch live in a static device array
+ * of 128 MiB that the library holds on every GPU it runs on until the process
+ * ends.  Problems whose dsa_workspace_size(p, DSA_OP_FORWARD) exceeds 128 MiB
+ * return DSA_ERR_UNSUPPORTED before any launch (the 64-sequence decode over
+ * 131,072 tokens needs about 118 MB; long prefills do not fit).  Every call
+ * on a device uses that device's one array: calls that overlap on one device
+ * (e.g. on two streams) race and give undefined results.  The first call on a
+ * device looks up the array's address there (no allocation).
+ */
+int dsa_forward_noalloc(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                        const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
+                        void* stream);
+
 /* Bytes of device workspace `op` needs for problem `p` (0 if none); returns
  * (size_t)-1 when the problem is invalid (dsa_last_error() says why). */
 size_t dsa_workspace_size(const dsa_problem* p, int op);

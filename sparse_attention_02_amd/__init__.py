@@ -82,12 +82,14 @@ def _load():
     L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_sparse_mla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.dsa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_warmup_kl.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_index_scores_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_sparse_mla_attn_ws,
               L.dsa_masked_mha_attn,
-              L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_warmup_target, L.dsa_warmup_kl,
+              L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_forward_noalloc, L.dsa_warmup_target,
+              L.dsa_warmup_kl,
               L.dsa_index_scores_bwd):
         f.restype = i32
     L.dsa_workspace_size.argtypes = [P, i32]
@@ -214,6 +216,14 @@ def dsa_forward(problem: Problem, q_idx, k_idx, w, q, kv, out, lse=None, indices
     _check(lib.dsa_forward(ctypes.byref(problem.c()), _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q),
                            _ptr(kv), _ptr(out), _ptr(lse), _ptr(indices), _ptr(workspace),
                            workspace_bytes, _stream(stream)))
+
+
+def dsa_forward_noalloc(problem: Problem, q_idx, k_idx, w, q, kv, out, lse=None, indices=None,
+                        stream=None) -> None:
+    """dsa_forward on the library's static scratch, for callers that cannot
+    allocate (include/dsa.h: dsa_forward_noalloc)."""
+    _check(lib.dsa_forward_noalloc(ctypes.byref(problem.c()), _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(q),
+                                   _ptr(kv), _ptr(out), _ptr(lse), _ptr(indices), _stream(stream)))
 
 
 def dsa_workspace_size(problem: Problem, op: int) -> int:

@@ -4,11 +4,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 
@@ -155,6 +157,78 @@ dsa::AttnArgs attn_args(const dsa_problem* p, const uint16_t* q, const uint16_t*
     a.part_lse = a.part_out + rows * a.nsplit * p->heads * p->d_latent;
   }
   return a;
+}
+
+int check_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                  const uint16_t* q, const uint16_t* kv, const float* out, const float* lse,
+                  const int32_t* indices) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_index(p)) return s;
+  if (int s = check_attn(p)) return s;
+  if (int s = check_ptr(q_idx, "q_idx", 16)) return s;
+  if (int s = check_ptr(k_idx, "k_idx", 16)) return s;
+  if (int s = check_ptr(w, "w", 4)) return s;
+  if (int s = check_ptr(q, "q", 16)) return s;
+  if (int s = check_ptr(kv, "kv", 16)) return s;
+  if (int s = check_ptr(out, "out", 16)) return s;
+  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_ALIGN, "lse is not 4-byte aligned");
+  if (indices && !aligned(indices, 16)) return fail(DSA_ERR_ALIGN, "indices is not 16-byte aligned");
+  return DSA_OK;
+}
+
+// Indexer -> top-k -> attention on `st`, with the scores, the selection (when
+// the caller does not take it) and the top-k and attention scratch carved from
+// `ws` (dsa_workspace_size(p, DSA_OP_FORWARD) bytes, 256-byte aligned).
+int run_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
+                uint8_t* ws, hipStream_t st) {
+  float* scores = (float*)ws;
+  int32_t* sel = indices ? indices : (int32_t*)(ws + round_up(scores_bytes(p)));
+  void* topk_ws = ws + round_up(scores_bytes(p)) + round_up(indices_bytes(p));
+  const size_t topk_bytes =
+      dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
+  void* attn_ws = (uint8_t*)topk_ws + round_up(topk_bytes);
+  if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
+                         "index_scores launch"))
+    return s;
+  if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel, topk_ws), st), "topk launch"))
+    return s;
+  return hip_status(
+      dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse, attn_ws, attn_ws_bytes(p)), st),
+      "sparse_mla_attn launch");
+}
+
+// Static scratch of dsa_forward_noalloc, for callers that cannot allocate.
+// Each device holds its own copy for the life of the process.  Host code uses
+// the device address hipGetSymbolAddress returns for the current device, never
+// the array's name.  No part of the forward's workspace needs to start at
+// zero, so the contents a previous call left are harmless; calls that overlap
+// on one device race for it.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_for_current_device(uint8_t** out) {
+  int dev = -1;
+  if (int s = hip_status(hipGetDevice(&dev), "hipGetDevice")) return s;
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device %d >= %d", dev, kMaxDevices);
+  uint8_t* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      void* addr = nullptr;
+      if (int s = hip_status(hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+        return s;
+      if (!addr || !aligned(addr, kAlign)) return fail(DSA_ERR_HIP, "scratch address %p not usable", addr);
+      ptr = (uint8_t*)addr;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return DSA_OK;
 }
 
 }  // namespace
@@ -356,39 +430,26 @@ int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
 int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
                 const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  if (int s = check_common(p)) return s;
-  if (int s = check_index(p)) return s;
-  if (int s = check_attn(p)) return s;
-  if (int s = check_ptr(q_idx, "q_idx", 16)) return s;
-  if (int s = check_ptr(k_idx, "k_idx", 16)) return s;
-  if (int s = check_ptr(w, "w", 4)) return s;
-  if (int s = check_ptr(q, "q", 16)) return s;
-  if (int s = check_ptr(kv, "kv", 16)) return s;
-  if (int s = check_ptr(out, "out", 16)) return s;
-  if (lse && !aligned(lse, 4)) return fail(DSA_ERR_ALIGN, "lse is not 4-byte aligned");
-  if (indices && !aligned(indices, 16)) return fail(DSA_ERR_ALIGN, "indices is not 16-byte aligned");
+  if (int s = check_forward(p, q_idx, k_idx, w, q, kv, out, lse, indices)) return s;
   const size_t need = dsa_workspace_size(p, DSA_OP_FORWARD);
   if (!workspace || workspace_bytes < need)
     return fail(DSA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need, workspace_bytes);
   if (!aligned(workspace, kAlign)) return fail(DSA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  return run_forward(p, q_idx, k_idx, w, q, kv, out, lse, indices, (uint8_t*)workspace, (hipStream_t)stream);
+}
 
-  uint8_t* ws = (uint8_t*)workspace;
-  float* scores = (float*)ws;
-  int32_t* sel = indices ? indices : (int32_t*)(ws + round_up(scores_bytes(p)));
-  void* topk_ws = ws + round_up(scores_bytes(p)) + round_up(indices_bytes(p));
-  const size_t topk_bytes =
-      dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
-  void* attn_ws = (uint8_t*)topk_ws + round_up(topk_bytes);
-  hipStream_t st = (hipStream_t)stream;
-
-  if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
-                         "index_scores launch"))
-    return s;
-  if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel, topk_ws), st), "topk launch"))
-    return s;
-  return hip_status(
-      dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse, attn_ws, attn_ws_bytes(p)), st),
-      "sparse_mla_attn launch");
+int dsa_forward_noalloc(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                        const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
+                        void* stream) {
+  if (int s = check_forward(p, q_idx, k_idx, w, q, kv, out, lse, indices)) return s;
+  const size_t need = dsa_workspace_size(p, DSA_OP_FORWARD);
+  if (need > kScratchBytes)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "forward_noalloc: this problem needs %zu bytes of scratch; the library's static scratch "
+                "holds %zu (use dsa_forward with a workspace)", need, kScratchBytes);
+  uint8_t* ws = nullptr;
+  if (int s = scratch_for_current_device(&ws)) return s;
+  return run_forward(p, q_idx, k_idx, w, q, kv, out, lse, indices, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

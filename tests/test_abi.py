@@ -260,3 +260,18 @@ def test_workspace_sizes_and_forward_checks():
     s, msg = _status(dsa.dsa_forward, MLA, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                      workspace=None, workspace_bytes=0, stream=0)
     assert s == -4, msg
+
+
+def test_forward_noalloc_checks():
+    """The allocation-free forward: exported, same argument checks as
+    dsa_forward, and problems whose forward workspace exceeds its 128 MiB of
+    static scratch are refused before any launch."""
+    dec = Problem(64, 1, 131072, 131071, 64, 128, 2048, 128, 512, 64)
+    assert dsa.workspace_size(dec, dsa.DSA_OP_FORWARD) <= 128 << 20
+    big = Problem(1, 32768, 32768, 0, 64, 128, 2048, 128, 512, 64)
+    s, msg = _status(dsa.dsa_forward_noalloc, big, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert s == -3 and "static scratch" in msg and str(128 << 20) in msg
+    s, msg = _status(dsa.dsa_forward_noalloc, dec, FAKE, None, FAKE, FAKE, FAKE, FAKE, stream=0)
+    assert s == -1 and "k_idx" in msg
+    s, msg = _status(dsa.dsa_forward_noalloc, dec, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, indices=FAKE + 4, stream=0)
+    assert s == -5 and "indices" in msg
