@@ -32,7 +32,9 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libdsa_inputs.so")
+# DSA_INPUTS_LIBRARY names another build (the sanitizer test's); unset, the
+# in-tree build is used.
+_LIB_PATH = os.environ.get("DSA_INPUTS_LIBRARY") or os.path.join(_HERE, "libdsa_inputs.so")
 
 # Tensor ids: each tensor of a workload draws from its own stream.
 TID_Q_IDX, TID_K_IDX, TID_W, TID_Q, TID_KV = 1, 2, 3, 4, 5

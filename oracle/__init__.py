@@ -28,7 +28,9 @@ import time
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# DSA_ORACLE_LIBRARY names another build (the sanitizer test's); unset, the
+# in-tree build is used.
+_LIB_PATH = os.environ.get("DSA_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 

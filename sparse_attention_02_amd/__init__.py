@@ -16,7 +16,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdsa.so")
+# DSA_LIBRARY names another build of the same library (the sanitizer test
+# loads a host-instrumented one); unset, the in-tree build is used.
+LIB_PATH = os.environ.get("DSA_LIBRARY") or os.path.join(_HERE, "libdsa.so")
 
 DSA_OP_INDEX_SCORES, DSA_OP_TOPK, DSA_OP_SPARSE_MLA_ATTN, DSA_OP_FORWARD = 0, 1, 2, 3
 DSA_OP_SPARSE_MLA_ATTN_BWD = 4

@@ -1,10 +1,13 @@
 """GPU parity of the sparse attention's backward over fixed indices (dq written,
 dkv accumulated) against the CPU oracle's double-precision gradients.
 
-Bar: max-abs error <= TOL * max|reference| per output.  dout, P and dZ are
-rounded to bf16 for the matrix cores (relative 2^-9 each) and the sums run in
-fp32, so the expected relative error is a few 1e-3; TOL = 2e-2 leaves room for
-the accumulation over 2048 entries."""
+Bar, per element: |gpu - ref| <= ROW_TOL * (largest |ref| of the element's
+row) + FLOOR * (largest |ref| of the tensor), a row being one (query, head)
+vector of dq or one token's row of dkv.  dout, P and dZ are rounded to bf16
+for the matrix cores (relative 2^-9 each) and the sums run in fp32; the
+largest per-row relative errors observed are ~8e-3 (dkv) and, for dq rows
+whose entries cancel to small values, up to ~0.2 of the row's own scale at
+~3e-3 of the tensor's, hence the floor on dq only."""
 import numpy as np
 import pytest
 import torch
@@ -16,7 +19,8 @@ from test_gpu_parity import EDGE
 
 pytestmark = pytest.mark.gpu
 
-TOL = 2e-2
+ROW_TOL = 2e-2
+FLOOR = {"dq": 6e-3, "dkv": 0.0}
 
 
 @pytest.fixture(scope="module")
@@ -38,19 +42,18 @@ def _bwd(dsa, prob, wl, d, indices, out, lse, dout):
 
 
 def _check(label, got, ref):
-    """The tensor-wide bound, plus the error of each element relative to the
-    largest reference magnitude of its own row (last axis: a (row, head)
-    vector of dq, a token's dkv row), logged."""
+    """Per-element bound: ROW_TOL times the largest reference magnitude of the
+    element's row (last axis), plus FLOOR times the tensor's largest."""
     e = np.abs(got - ref)
-    err = float(e.max())
     scale = float(np.abs(ref).max())
     rowmax = np.abs(ref).max(axis=-1, keepdims=True)
-    live = rowmax[..., 0] > 0
-    per_row = (e.max(axis=-1)[live] / rowmax[..., 0][live]) if live.any() else np.zeros(1)
-    log(f"[{label}] max-abs {err:.3e} of max|ref| {scale:.3e} (relative {err / max(scale, 1e-30):.2e}); "
-        f"per-row relative max {per_row.max():.2e}, p99.9 {np.quantile(per_row, 0.999):.2e}, "
-        f"rows {per_row.size}; dead rows max-abs {float(e.max(axis=-1)[~live].max()) if (~live).any() else 0:.1e}")
-    assert err <= TOL * scale + 1e-6, f"{label}: {err} > {TOL} * {scale}"
+    floor = FLOOR["dq" if "dq" in label else "dkv"] * scale
+    bound = np.broadcast_to(ROW_TOL * rowmax + floor + 1e-6, e.shape)
+    ratio = e / bound
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    log(f"[{label}] max-abs {float(e.max()):.3e} of max|ref| {scale:.3e}; worst error/bound "
+        f"{float(ratio.max()):.3f} at {tuple(int(i) for i in worst)}")
+    assert float(ratio.max()) <= 1.0, f"{label}: error {float(e[worst]):.3e} > bound {float(bound[worst]):.3e} at {worst}"
 
 
 def _run_case(dsa, wl, rows_with_grad=None, indices_np=None, seed=0):

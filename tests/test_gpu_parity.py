@@ -291,3 +291,79 @@ def test_topk_remaining_paths(dsa, k, Lk, Lq, B):
         ref = oracle.topk(np.ascontiguousarray(s[b]), pos, k)
         np.testing.assert_array_equal(got[b], ref)
     np.testing.assert_array_equal(got[-1, -1], np.arange(k))
+
+
+@pytest.mark.parametrize("shape", ["tiny", "mla"])
+def test_attention_invalid_entries_masked_chunks_and_empty_rows(dsa, shape):
+    """Hand-built selections through dsa_sparse_mla_attn at both latent shapes:
+    -1 and out-of-range entries, unsorted lists, rows whose valid entries sit
+    only in the last chunk (leading chunks wholly invalid), and an empty row."""
+    if shape == "tiny":
+        wl = dsa_inputs.Workload("inv_t", 23, 1, 6, 300, 294, 4, 32, 96, 16, 64, 16)
+    else:
+        wl = dsa_inputs.Workload("inv_m", 24, 1, 6, 300, 294, 4, 32, 96, 128, 512, 64)
+    log(f"[invalid {shape}] H={wl.heads} Dv={wl.d_latent}+{wl.d_rope} k={wl.topk}")
+    inp = Inputs.make(wl)
+    rng = np.random.default_rng(4)
+    k = wl.topk
+    idx = np.full((1, 6, k), -1, np.int32)
+    idx[0, 0, :70] = np.sort(rng.choice(300, 70, replace=False))
+    idx[0, 1, ::3] = rng.choice(300, 32, replace=False)          # unsorted, -1 in between
+    idx[0, 2, :6] = [3, 500, -7, 299, 2 ** 30, 0]                  # out-of-range entries skipped
+    idx[0, 3, 64:] = np.arange(32)                                 # only the last chunk valid
+    idx[0, 5, k - 1] = 7                                           # one valid entry in the tail
+    # row 4 stays all -1: out = 0, lse = -inf
+    prob = dsa.Problem.from_workload(wl)
+    d = inp.device()
+    out = torch.full((1, 6, wl.heads, wl.d_latent), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((1, 6, wl.heads), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_sparse_mla_attn(prob, d["q"], d["kv"], dev(idx), out, lse)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.sparse_mla_attn(inp.kv, inp.q, idx[0], np.zeros(6, np.int32), wl.d_latent,
+                                          wl.softmax_scale)
+    o = out.cpu().numpy()[0]
+    l = lse.cpu().numpy()[0]
+    assert np.abs(o - ref_o).max() <= ATOL
+    assert (o[4] == 0).all() and np.isneginf(l[4]).all()
+    fin = np.isfinite(ref_l)
+    assert np.array_equal(fin, np.isfinite(l))
+    assert np.abs(l[fin] - ref_l[fin]).max() <= ATOL
+
+
+def test_attention_score_range_far_above_the_first_chunk(dsa):
+    """Late selected tokens whose scores exceed every earlier one by far more
+    than 2^32 in probability (a latent row that is a large multiple of the
+    query), at the MLA shape: the result must still be the softmax of the
+    whole selection, for split and unsplit rows."""
+    B, Lk, k = 3, 4000, 2048
+    wl = dsa_inputs.Workload("range", 33, B, 1, Lk, Lk - 1, 4, 32, k, 128, 512, 64)
+    log(f"[score range] B={B} Lk={Lk} k={k}")
+    inp = Inputs.make(wl)
+    kv = inp.kv.copy()
+    q = inp.q.copy()
+    rng = np.random.default_rng(8)
+    idx = np.sort(np.stack([rng.choice(Lk, k, replace=False) for _ in range(B)]), axis=1).astype(np.int32)
+    qv = torch.from_numpy(q.view(np.int16).copy()).view(torch.bfloat16).float()
+    for b_ in range(B):
+        # row b_: a selected token near the end aligned with head 5's query, 8x larger
+        s_big = int(idx[b_, k - 40 + 10 * b_])
+        kv[b_, s_big] = (8.0 * qv[b_, 5]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    prob = dsa.Problem.from_workload(wl)
+    kv_d = dev(kv)
+    q_d = dev(q)
+    ref_o, ref_l = oracle.sparse_mla_attn(kv, q, idx, np.arange(B, dtype=np.int32), 512, wl.softmax_scale)
+    assert ref_l[:, 5].min() > 100.0  # the big score dominates head 5
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
+    for use_ws in (False, True):
+        out = torch.empty((B, 1, 128, 512), dtype=torch.float32, device="cuda")
+        lse = torch.empty((B, 1, 128), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        dsa.dsa_sparse_mla_attn_ws(prob, q_d, kv_d, dev(idx.reshape(B, 1, k)), out, lse, ws if use_ws else None,
+                                   ws_bytes if use_ws else 0)
+        torch.cuda.synchronize()
+        o = out.cpu().numpy()[:, 0]
+        l = lse.cpu().numpy()[:, 0]
+        err = np.abs(o - ref_o).max()
+        lerr = np.abs(l - ref_l).max()
+        log(f"[score range] split={use_ws}: max-abs {err:.2e}, lse {lerr:.2e} (lse up to {ref_l.max():.1f})")
+        assert err <= ATOL and lerr <= ATOL * max(1.0, float(np.abs(ref_l).max()) / 100.0)

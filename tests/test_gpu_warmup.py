@@ -193,20 +193,21 @@ def test_warmup_chain_indexer_target_kl(dsa, name):
 # Gradients of the indexer scores with respect to q_I, w and k_I
 # ---------------------------------------------------------------------------
 
-IB_TOL = 1e-2  # dq_I, dk_I: dscores * w is rounded to bf16 (2^-9) for the products
-DW_TOL = 1e-5  # dw: fp32 sums of exact ReLU(u) times fp32 dscores
+IB_TOL = 1.5e-2  # dq_I, dk_I: dscores * w is rounded to bf16 (2^-9) for the products; worst row seen ~5e-3
+DW_TOL = 1e-5    # dw: fp32 sums of exact ReLU(u) times fp32 dscores; worst row seen ~7e-7
 
 
 def _ib_check(label, got, ref, tol):
+    """Per-element bound: tol times the largest reference magnitude of the
+    element's row (last axis: one (query, head) vector of dq_I or dw's row of
+    heads, one token's row of dk_I)."""
     e = np.abs(got - ref)
-    err = float(e.max())
-    scale = float(np.abs(ref).max())
-    rowmax = np.abs(ref).max(axis=-1)
-    live = rowmax > 0
-    per_row = e.max(axis=-1)[live] / rowmax[live] if live.any() else np.zeros(1)
-    log(f"[{label}] max-abs {err:.3e} of max|ref| {scale:.3e} (relative {err / max(scale, 1e-30):.2e}); "
-        f"per-row relative max {per_row.max():.2e}, p99.9 {np.quantile(per_row, 0.999):.2e}, rows {per_row.size}")
-    assert err <= tol * scale + 1e-7, f"{label}: {err} > {tol} * {scale}"
+    rowmax = np.abs(ref).max(axis=-1, keepdims=True)
+    bound = tol * rowmax + 1e-7
+    ratio = e / bound
+    log(f"[{label}] max-abs {float(e.max()):.3e} of max|ref| {float(np.abs(ref).max()):.3e}; "
+        f"worst error/bound {float(ratio.max()):.3f}")
+    assert float(ratio.max()) <= 1.0, f"{label}: worst error/bound {float(ratio.max()):.3f}"
 
 
 def _index_bwd_case(dsa, wl, rows=None, seed=5):
