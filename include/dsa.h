@@ -32,6 +32,8 @@
  *   dsa_masked_mha_attn  the same attention computed densely over each
  *                        query's causal range with the non-selected tokens
  *                        masked: the masked mode for short prefill.
+ *   dsa_index_topk       the indexer and the top-k together, without
+ *                        materialising every score of long rows.
  *   dsa_forward          the three stages in order on one stream.
  *
  * Conventions shared by every entry point
@@ -98,7 +100,8 @@ enum dsa_op {
   DSA_OP_TOPK = 1,
   DSA_OP_SPARSE_MLA_ATTN = 2,
   DSA_OP_FORWARD = 3,
-  DSA_OP_SPARSE_MLA_ATTN_BWD = 4
+  DSA_OP_SPARSE_MLA_ATTN_BWD = 4,
+  DSA_OP_INDEX_TOPK = 5
 };
 
 /*
@@ -146,6 +149,31 @@ int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* 
  */
 int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
              size_t workspace_bytes, void* stream);
+
+/*
+ * dsa_index_scores followed by dsa_topk, without necessarily materialising
+ * the scores: the selection of the lightning indexer ("DeepSeek V3.2 and the
+ * lightning indexer", "How the lightning indexer works": score every
+ * preceding token, keep the k best per query).  The result is bit-identical
+ * to the two calls.
+ *
+ *   q_idx, k_idx, w  as for dsa_index_scores
+ *   indices  [B, Lq, k] int32 output, as for dsa_topk
+ *   workspace: at least dsa_workspace_size(p, DSA_OP_INDEX_TOPK) bytes,
+ *              256-byte aligned; contents on return are unspecified.
+ * When rows exceed 32768 keys in a problem of at least 8 queries per
+ * sequence, the scores of one key in 16 (32, 64, ... for rows past 512K keys)
+ * give each row a threshold, the indexer then writes only the keys at or
+ * above it (a little more than k per row instead of the whole row) and the
+ * top-k selects among those; a row whose sample misled the threshold (fewer
+ * than k keys above it, or more than its candidate slots hold, e.g. heavy
+ * ties) is recomputed through its full score row, so every row's result is
+ * exact.  Otherwise (decode, rows up to 32768 keys) it runs the two stages as
+ * they are.  The workspace holds the full score matrix either way
+ * (4 * B * Lq * Lk bytes, for the recomputed rows).
+ */
+int dsa_index_topk(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                   int32_t* indices, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Sparse attention, MQA mode of MLA, over the selected latents.
@@ -329,9 +357,9 @@ int dsa_masked_mha_attn(const dsa_problem* p, const uint16_t* q, const uint16_t*
  * DSA_OP_FORWARD) bytes, 256-byte aligned).  `indices` may be NULL; when given
  * ([B, Lq, k] int32) it receives the selection, otherwise the selection is
  * kept in the workspace, together with the top-k and attention scratch.
- * Results are bit-identical to dsa_index_scores, dsa_topk and
- * dsa_sparse_mla_attn_ws called with workspaces of the sizes
- * dsa_workspace_size() reports for them.
+ * It runs dsa_index_topk, then dsa_sparse_mla_attn_ws; results are
+ * bit-identical to dsa_index_scores, dsa_topk and dsa_sparse_mla_attn_ws
+ * called with workspaces of the sizes dsa_workspace_size() reports for them.
  */
 int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
                 const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,

@@ -22,6 +22,7 @@ LIB_PATH = os.environ.get("DSA_LIBRARY") or os.path.join(_HERE, "libdsa.so")
 
 DSA_OP_INDEX_SCORES, DSA_OP_TOPK, DSA_OP_SPARSE_MLA_ATTN, DSA_OP_FORWARD = 0, 1, 2, 3
 DSA_OP_SPARSE_MLA_ATTN_BWD = 4
+DSA_OP_INDEX_TOPK = 5
 STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_UNSUPPORTED",
           -4: "DSA_ERR_WORKSPACE", -5: "DSA_ERR_ALIGN", -6: "DSA_ERR_HIP"}
 
@@ -79,6 +80,7 @@ def _load():
     vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
     L.dsa_index_scores.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_topk.argtypes = [P, vp, vp, vp, sz, vp]
+    L.dsa_index_topk.argtypes = [P, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_sparse_mla_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_sparse_mla_attn_ws.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     L.dsa_masked_mha_attn.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -88,7 +90,7 @@ def _load():
     L.dsa_warmup_target.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.dsa_warmup_kl.argtypes = [P, vp, vp, vp, vp, vp]
     L.dsa_index_scores_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
-    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_sparse_mla_attn, L.dsa_sparse_mla_attn_ws,
+    for f in (L.dsa_index_scores, L.dsa_topk, L.dsa_index_topk, L.dsa_sparse_mla_attn, L.dsa_sparse_mla_attn_ws,
               L.dsa_masked_mha_attn,
               L.dsa_sparse_mla_attn_bwd, L.dsa_forward, L.dsa_forward_noalloc, L.dsa_warmup_target,
               L.dsa_warmup_kl,
@@ -148,6 +150,17 @@ def dsa_topk(problem: Problem, scores, indices, workspace=None, workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check(lib.dsa_topk(ctypes.byref(problem.c()), _ptr(scores), _ptr(indices), _ptr(workspace),
                         workspace_bytes, _stream(stream)))
+
+
+def dsa_index_topk(problem: Problem, q_idx, k_idx, w, indices, workspace, workspace_bytes: int = 0,
+                   stream=None) -> None:
+    """Indexer scores and top-k without necessarily materialising the scores
+    (include/dsa.h: dsa_index_topk); workspace from
+    dsa_workspace_size(problem, DSA_OP_INDEX_TOPK)."""
+    if workspace is not None and not isinstance(workspace, int) and workspace_bytes == 0:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dsa_index_topk(ctypes.byref(problem.c()), _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(indices),
+                              _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def dsa_sparse_mla_attn(problem: Problem, q, kv, indices, out, lse=None, stream=None) -> None:

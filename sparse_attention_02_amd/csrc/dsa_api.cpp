@@ -126,6 +126,8 @@ dsa::IndexArgs index_args(const dsa_problem* p, const uint8_t* q_idx, const uint
   a.q_idx = q_idx; a.k_idx = k_idx; a.w = w; a.scores = scores;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start;
   a.HI = p->idx_heads; a.dI = p->idx_dim;
+  a.key_stride = 1;
+  a.out_ld = p->kv_len;
   return a;
 }
 
@@ -133,7 +135,95 @@ dsa::TopkArgs topk_args(const dsa_problem* p, const float* scores, int32_t* indi
   dsa::TopkArgs a{};
   a.scores = scores; a.indices = indices; a.workspace = ws;
   a.B = p->batch; a.Lq = p->q_len; a.Lk = p->kv_len; a.q_start = p->q_start; a.k = p->topk;
+  a.seg_cap = p->topk;
   return a;
+}
+
+// Workspace of dsa_index_topk: the plain path's score matrix and top-k
+// scratch (also the fused path's fallback), and for the fused path the
+// sampled scores, the thresholds, the candidate slots, their counts and the
+// fallback flags.  Offsets are 256-byte aligned.
+struct IndexTopkLayout {
+  dsa::FusedPlan f;
+  size_t scores, topk_ws, sample, thresh, cand_key, cand_idx, count, flags, total;
+};
+
+IndexTopkLayout index_topk_layout(const dsa_problem* p) {
+  IndexTopkLayout L{};
+  L.f = dsa::fused_plan(p->batch, p->q_len, p->kv_len, p->q_start, p->idx_heads, p->idx_dim, p->topk);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round_up(bytes);
+    return o;
+  };
+  const size_t rows = (size_t)p->batch * p->q_len;
+  L.scores = take(scores_bytes(p));
+  L.topk_ws = take(dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk));
+  if (L.f.use) {
+    const size_t slots = rows * L.f.n_splits * L.f.cap_s;
+    L.sample = take(rows * L.f.ls * sizeof(float));
+    L.thresh = take(rows * sizeof(uint32_t));
+    L.cand_key = take(slots * sizeof(uint32_t));
+    L.cand_idx = take(slots * sizeof(int32_t));
+    L.count = take(rows * L.f.n_splits * sizeof(int32_t));
+    L.flags = take(rows * sizeof(int32_t));
+  }
+  L.total = off;
+  return L;
+}
+
+// Indexer scores and top-k into `indices`.  Plain: the scores go to the
+// workspace and the top-k reads them.  Fused (long rows, prefill shape): the
+// indexer scores a key sample, a threshold per row is taken from it, the
+// indexer writes only the (key, index) pairs at or above the threshold, and
+// the top-k selects among those; rows whose candidates cannot be trusted are
+// redone by the plain path, restricted to them.
+int run_index_topk(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                   int32_t* indices, uint8_t* ws, hipStream_t st) {
+  const IndexTopkLayout L = index_topk_layout(p);
+  float* scores = (float*)(ws + L.scores);
+  void* topk_ws = ws + L.topk_ws;
+  if (!L.f.use) {
+    if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
+                           "index_scores launch"))
+      return s;
+    return hip_status(dsa::launch_topk(topk_args(p, scores, indices, topk_ws), st), "topk launch");
+  }
+  float* sample = (float*)(ws + L.sample);
+  uint32_t* thresh = (uint32_t*)(ws + L.thresh);
+  uint32_t* cand_key = (uint32_t*)(ws + L.cand_key);
+  int32_t* cand_idx = (int32_t*)(ws + L.cand_idx);
+  int32_t* count = (int32_t*)(ws + L.count);
+  int32_t* flags = (int32_t*)(ws + L.flags);
+  dsa::IndexArgs sa = index_args(p, q_idx, k_idx, w, sample);
+  sa.key_stride = L.f.stride;
+  sa.out_ld = L.f.ls;
+  if (int s = hip_status(dsa::launch_index_scores(sa, st), "sampled index_scores launch")) return s;
+  if (int s = hip_status(dsa::launch_fused_threshold(sample, thresh, p->batch, p->q_len, p->kv_len, p->q_start,
+                                                     p->topk, L.f.stride, L.f.ls, st),
+                         "threshold launch"))
+    return s;
+  dsa::IndexArgs fa = index_args(p, q_idx, k_idx, w, nullptr);
+  fa.thresh = thresh;
+  fa.cand_key = cand_key;
+  fa.cand_idx = cand_idx;
+  fa.row_count = count;
+  fa.cap_s = L.f.cap_s;
+  fa.n_splits = L.f.n_splits;
+  if (int s = hip_status(dsa::launch_index_scores(fa, st), "filtering index_scores launch")) return s;
+  dsa::TopkArgs ta = topk_args(p, nullptr, indices, nullptr);
+  ta.nseg = L.f.n_splits;
+  ta.seg_cap = L.f.cap_s;
+  ta.cand_key = cand_key;
+  ta.cand_idx = cand_idx;
+  if (int s = hip_status(dsa::launch_fused_select(ta, count, flags, st), "fused select launch")) return s;
+  dsa::IndexArgs pa = index_args(p, q_idx, k_idx, w, scores);
+  pa.only_rows = flags;
+  if (int s = hip_status(dsa::launch_index_scores(pa, st), "fallback index_scores launch")) return s;
+  dsa::TopkArgs tb = topk_args(p, scores, indices, topk_ws);
+  tb.only_rows = flags;
+  return hip_status(dsa::launch_topk(tb, st), "fallback topk launch");
 }
 
 size_t attn_ws_bytes(const dsa_problem* p) {
@@ -182,17 +272,10 @@ int check_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_i
 int run_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
                 const uint16_t* q, const uint16_t* kv, float* out, float* lse, int32_t* indices,
                 uint8_t* ws, hipStream_t st) {
-  float* scores = (float*)ws;
-  int32_t* sel = indices ? indices : (int32_t*)(ws + round_up(scores_bytes(p)));
-  void* topk_ws = ws + round_up(scores_bytes(p)) + round_up(indices_bytes(p));
-  const size_t topk_bytes =
-      dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk);
-  void* attn_ws = (uint8_t*)topk_ws + round_up(topk_bytes);
-  if (int s = hip_status(dsa::launch_index_scores(index_args(p, q_idx, k_idx, w, scores), st),
-                         "index_scores launch"))
-    return s;
-  if (int s = hip_status(dsa::launch_topk(topk_args(p, scores, sel, topk_ws), st), "topk launch"))
-    return s;
+  const size_t it_bytes = index_topk_layout(p).total;
+  int32_t* sel = indices ? indices : (int32_t*)(ws + it_bytes);
+  void* attn_ws = ws + it_bytes + round_up(indices_bytes(p));
+  if (int s = run_index_topk(p, q_idx, k_idx, w, sel, ws, st)) return s;
   return hip_status(
       dsa::launch_sparse_mla_attn(attn_args(p, q, kv, sel, out, lse, attn_ws, attn_ws_bytes(p)), st),
       "sparse_mla_attn launch");
@@ -263,11 +346,12 @@ size_t dsa_workspace_size(const dsa_problem* p, int op) {
       return check_attn(p) ? bad : attn_ws_bytes(p);
     case DSA_OP_SPARSE_MLA_ATTN_BWD:
       return check_attn(p) || check_bwd_size(p) ? bad : bwd_ws_bytes(p);
+    case DSA_OP_INDEX_TOPK:
+      if (check_index(p) || check_topk(p)) return bad;
+      return index_topk_layout(p).total;
     case DSA_OP_FORWARD:
       if (check_index(p) || check_attn(p)) return bad;
-      return round_up(scores_bytes(p)) + round_up(indices_bytes(p)) +
-             round_up(dsa::topk_workspace_bytes(p->batch, p->q_len, p->q_start, p->kv_len, p->topk)) +
-             round_up(attn_ws_bytes(p));
+      return index_topk_layout(p).total + round_up(indices_bytes(p)) + round_up(attn_ws_bytes(p));
     default:
       fail(DSA_ERR_SHAPE, "unknown op %d", op);
       return bad;
@@ -301,6 +385,22 @@ int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* 
   return hip_status(dsa::launch_topk(topk_args(p, scores, indices, need > 0 ? workspace : nullptr),
                                      (hipStream_t)stream),
                     "topk launch");
+}
+
+int dsa_index_topk(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx, const float* w,
+                   int32_t* indices, void* workspace, size_t workspace_bytes, void* stream) {
+  if (int s = check_common(p)) return s;
+  if (int s = check_index(p)) return s;
+  if (int s = check_topk(p)) return s;
+  if (int s = check_ptr(q_idx, "q_idx", 16)) return s;
+  if (int s = check_ptr(k_idx, "k_idx", 16)) return s;
+  if (int s = check_ptr(w, "w", 4)) return s;
+  if (int s = check_ptr(indices, "indices", 4)) return s;
+  const size_t need = index_topk_layout(p).total;
+  if (!workspace || workspace_bytes < need)
+    return fail(DSA_ERR_WORKSPACE, "index_topk needs %zu workspace bytes, got %zu", need, workspace_bytes);
+  if (!aligned(workspace, kAlign)) return fail(DSA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  return run_index_topk(p, q_idx, k_idx, w, indices, (uint8_t*)workspace, (hipStream_t)stream);
 }
 
 int dsa_sparse_mla_attn_ws(const dsa_problem* p, const uint16_t* q, const uint16_t* kv,

@@ -47,6 +47,15 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
   return u >> 16;
 }
 
+// Order-preserving 32-bit key of an fp32 score (larger score, larger key);
+// -0 is folded onto +0 so the two tie.  Every score but the NaN with all bits
+// set maps to a key >= 1, so 0 can mark an absent candidate.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

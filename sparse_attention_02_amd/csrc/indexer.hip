@@ -64,8 +64,11 @@ constexpr int kKeysPerWave = 64;
 // starts at +0.
 __device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.0f); }
 
-template <int NKL, int NHG, bool FULLD, int NW, int kQPW>
+// FILTER: instead of the scores, write the candidates above the row's
+// threshold (IndexArgs, "Filtering"); the prefill shape (one query per wave).
+template <int NKL, int NHG, bool FULLD, int NW, int kQPW, bool FILTER>
 __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
+  static_assert(!FILTER || (NKL == 1 && kQPW == 1), "filtering runs one query per wave");
   constexpr int kThreads = 64 * NW;
   constexpr int NQG = NW / NKL;         // query groups per block
   constexpr int QT = kQPW * NQG;        // queries per block
@@ -86,11 +89,32 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
 
   const int t_first = tile * QT;
   const int t_last = min(t_first + QT, a.Lq) - 1;
-  const int kv_end = min(a.Lk, a.q_start + t_last + 1);
+  if (a.only_rows) {
+    bool any = false;
+    for (int t = t_first; t <= t_last; ++t) any |= a.only_rows[(size_t)b * a.Lq + t] != 0;
+    if (!any) return;
+  }
+  // keys are s = stride * s' for s' < ls; a tile needs s' <= (its last position) / stride
+  const int stride = a.key_stride;
+  const int ls = (a.Lk + stride - 1) / stride;
+  const int kv_end = min(ls, (a.q_start + t_last) / stride + 1);
   const int nst_total = (kv_end + KS - 1) / KS;
   const int st_begin = (int)((long long)nst_total * split / a.n_splits);
   const int st_end = (int)((long long)nst_total * (split + 1) / a.n_splits);
-  if (st_begin >= st_end) return;
+  if (st_begin >= st_end) {
+    if constexpr (FILTER) {  // an empty split still reports: no candidates
+      const int t = t_first + qgroup * kQPW;
+      if (t < a.Lq) {
+        const size_t r = (size_t)b * a.Lq + t;
+        for (int j = lane; j < a.cap_s; j += 64) {
+          a.cand_key[(r * a.n_splits + split) * a.cap_s + j] = 0u;
+          a.cand_idx[(r * a.n_splits + split) * a.cap_s + j] = -1;
+        }
+        if (lane == 0) a.row_count[r * a.n_splits + split] = 0;
+      }
+    }
+    return;
+  }
 
   const int dI = a.dI;
   constexpr bool SWZ = NKL == 1;        // prefill: swizzled 128-byte rows (see above)
@@ -141,8 +165,8 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
     for (int j = 0; j < kMaxPieces; ++j) {
       const int p = threadIdx.x + j * kThreads;
       if (p < stage_pieces) {
-        const int key = min(kbase + p / pieces_per_row, a.Lk - 1);
-        pf[j] = *(const v4i*)(kseq + (size_t)key * dI + 16 * (p % pieces_per_row));
+        const int key = min(kbase + p / pieces_per_row, ls - 1);
+        pf[j] = *(const v4i*)(kseq + (size_t)key * stride * dI + 16 * (p % pieces_per_row));
       }
     }
   };
@@ -157,6 +181,30 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
       }
     }
   };
+
+  // last (sampled) key of each query row: s' <= lim, or none for absent rows
+  int lim[kQPW];
+#pragma unroll
+  for (int q = 0; q < kQPW; ++q) {
+    const int t = t_first + qgroup * kQPW + q;
+    lim[q] = t < a.Lq ? min(ls - 1, (a.q_start + t) / stride) : -1;
+  }
+  // filtering: this wave's threshold (as the score whose order key it is: a
+  // score passes iff it is >= that value, -0 and +0 alike) and candidate slots
+  int cursor = 0;
+  float thr = __builtin_nanf("");
+  uint32_t* fck = nullptr;
+  int32_t* fci = nullptr;
+  const int frow_t = t_first + qgroup * kQPW;
+  if constexpr (FILTER) {
+    if (frow_t < a.Lq) {
+      const size_t r = (size_t)b * a.Lq + frow_t;
+      const uint32_t tk = a.thresh[r];
+      thr = __uint_as_float((tk & 0x80000000u) ? (tk & 0x7FFFFFFFu) : ~tk);
+      fck = a.cand_key + (r * a.n_splits + split) * a.cap_s;
+      fci = a.cand_idx + (r * a.n_splits + split) * a.cap_s;
+    }
+  }
 
   load_stage(st_begin);
   store_stage(0);
@@ -231,41 +279,67 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
       const auto b01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(k0), __float_as_uint(k1), false, false);
       const float fin = __uint_as_float(b01[0]) + __uint_as_float(b01[1]);
       const int t = t_first + qgroup * kQPW + q;
-      if (t < a.Lq && key <= a.q_start + t && key < a.Lk)
-        a.scores[((size_t)b * a.Lq + t) * a.Lk + key] = fin;
+      const bool valid = key <= lim[q];
+      if constexpr (FILTER) {
+        // the row's keys >= its threshold, in ascending index order
+        const bool keep = valid && fin >= thr;
+        const uint64_t m = __ballot(keep);
+        if (m) {
+          const int slot = cursor + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (keep && slot < a.cap_s) {
+            fck[slot] = max(order_key(fin), 1u);
+            fci[slot] = key;
+          }
+          cursor += __builtin_popcountll(m);
+        }
+      } else if (valid) {
+        a.scores[((size_t)b * a.Lq + t) * a.out_ld + key] = fin;
+      }
     }
 
     if (st + 1 < st_end) store_stage(buf ^ 1);
     __syncthreads();
   }
+  if constexpr (FILTER) {
+    if (frow_t < a.Lq) {
+      for (int j = min(cursor, a.cap_s) + lane; j < a.cap_s; j += 64) {
+        fck[j] = 0u;
+        fci[j] = -1;
+      }
+      if (lane == 0) a.row_count[((size_t)b * a.Lq + frow_t) * a.n_splits + split] = cursor;
+    }
+  }
 }
 
 }  // namespace
 
-hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
-  IndexArgs a = args_in;
+// Long key ranges are split over several blocks.  The splits write disjoint
+// key ranges, but each one pays its own prologue (query operands, head
+// weights, a first stage load that nothing hides), so a split is worth it
+// only while the chip is under-filled or the grid's last round is.
+//  - decode: one round of resident blocks (a 256-key stage pair takes
+//    ~74 KB of LDS, so two blocks per CU): more rounds only add prologues.
+//  - prefill: first at least two rounds (~5 blocks per CU) while a split
+//    keeps >= 16 stages; then, because rows of equal length (chunked
+//    prefill) end together and leave the last round part-empty, up to 32768
+//    blocks while a split keeps >= 256 stages.  Causal rows from position 0
+//    need no such help: their lengths differ and the longest start first.
+// Measured on the 64 x 128 indexer: decode over 64 x 128K keys is fastest at
+// 8 splits, over 4 x 1M at 128; prefill over 4K at 2, over 32K at 1, 8K new
+// tokens of 128K at 4-8, 4K of 1M at 32.  With key sampling the stages are
+// counted in sampled keys.
+int index_splits(const IndexArgs& a) {
   const bool decode = a.Lq < 8;
   const int QT = decode ? kDecodeQPW * kDecodeWaves / 4 : kPrefillQPW * kPrefillWaves;
   const int KS = decode ? 4 * kKeysPerWave : kKeysPerWave;
-  a.n_qtiles = (a.Lq + QT - 1) / QT;
-  // Long key ranges are split over several blocks.  The splits write disjoint
-  // key ranges, but each one pays its own prologue (query operands, head
-  // weights, a first stage load that nothing hides), so a split is worth it
-  // only while the chip is under-filled or the grid's last round is.
-  //  - decode: one round of resident blocks (a 256-key stage pair takes
-  //    ~74 KB of LDS, so two blocks per CU): more rounds only add prologues.
-  //  - prefill: first at least two rounds (~5 blocks per CU) while a split
-  //    keeps >= 16 stages; then, because rows of equal length (chunked
-  //    prefill) end together and leave the last round part-empty, up to 32768
-  //    blocks while a split keeps >= 256 stages.  Causal rows from position 0
-  //    need no such help: their lengths differ and the longest start first.
-  // Measured on the 64 x 128 indexer: decode over 64 x 128K keys is fastest at
-  // 8 splits, over 4 x 1M at 128; prefill over 4K at 2, over 32K at 1, 8K new
-  // tokens of 128K at 4-8, 4K of 1M at 32.
-  const long long tiles = (long long)a.B * a.n_qtiles;
-  const int max_st = (a.Lk + KS - 1) / KS;
-  // Stages of an average tile: a tile's keys end at its last position.
-  const long long avg_st = ((long long)a.q_start + (a.Lq + 1) / 2 + KS - 1) / KS;
+  const int stride = a.key_stride;
+  const long long n_qtiles = (a.Lq + QT - 1) / QT;
+  const long long tiles = (long long)a.B * n_qtiles;
+  const int ls = (a.Lk + stride - 1) / stride;
+  const int max_st = (ls + KS - 1) / KS;
+  // stages of an average tile: a tile's keys end at its last position
+  const long long avg_st = (((long long)a.q_start + (a.Lq + 1) / 2) / stride + KS - 1) / KS;
   int splits = 1;
   auto grow = [&](long long blocks, long long min_stages) {
     while (tiles * splits < blocks && splits * 2 <= max_st && avg_st >= 2LL * splits * min_stages)
@@ -278,26 +352,43 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
     grow(2 * 256 * 5, 16);
     grow(32768, 256);
   }
-  a.n_splits = splits;
+  return splits;
+}
+
+hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
+  IndexArgs a = args_in;
+  const bool decode = a.Lq < 8;
+  const bool filter = a.thresh != nullptr;
+  if (filter && decode) return hipErrorInvalidValue;
+  const int QT = decode ? kDecodeQPW * kDecodeWaves / 4 : kPrefillQPW * kPrefillWaves;
+  const int KS = decode ? 4 * kKeysPerWave : kKeysPerWave;
+  a.n_qtiles = (a.Lq + QT - 1) / QT;
+  // a filtering launch uses the split count its candidate slots were sized for
+  if (!filter) a.n_splits = index_splits(a);
   const size_t smem = 2 * (size_t)KS * (decode ? a.dI + 16 : 128);  // two stages of key rows
-  const dim3 grid((unsigned)(tiles * splits));
+  const dim3 grid((unsigned)((long long)a.B * a.n_qtiles * a.n_splits));
   const int nhg = (a.HI + 15) >> 4;
   const bool full = a.dI == 128;
-#define DSA_K1(NKL, NHG, NW, QPW)                                    \
-  (full ? (const void*)index_scores_kernel<NKL, NHG, true, NW, QPW> \
-        : (const void*)index_scores_kernel<NKL, NHG, false, NW, QPW>)
+#define DSA_K1(NKL, NHG, NW, QPW, F)                                    \
+  (full ? (const void*)index_scores_kernel<NKL, NHG, true, NW, QPW, F> \
+        : (const void*)index_scores_kernel<NKL, NHG, false, NW, QPW, F>)
   const void* kern;
   int threads;
   if (decode) {
     threads = 64 * kDecodeWaves;
-    kern = nhg == 1   ? DSA_K1(4, 1, kDecodeWaves, kDecodeQPW)
-           : nhg == 2 ? DSA_K1(4, 2, kDecodeWaves, kDecodeQPW)
-                      : DSA_K1(4, 4, kDecodeWaves, kDecodeQPW);
+    kern = nhg == 1   ? DSA_K1(4, 1, kDecodeWaves, kDecodeQPW, false)
+           : nhg == 2 ? DSA_K1(4, 2, kDecodeWaves, kDecodeQPW, false)
+                      : DSA_K1(4, 4, kDecodeWaves, kDecodeQPW, false);
+  } else if (filter) {
+    threads = 64 * kPrefillWaves;
+    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, true)
+           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, true)
+                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, true);
   } else {
     threads = 64 * kPrefillWaves;
-    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW)
-           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW)
-                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW);
+    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, false)
+           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, false)
+                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, false);
   }
 #undef DSA_K1
   if (smem > 64 * 1024) {

@@ -12,9 +12,27 @@ struct IndexArgs {
   const uint8_t* q_idx;  // [B, Lq, HI, dI] e4m3fn
   const uint8_t* k_idx;  // [B, Lk, dI]     e4m3fn
   const float* w;        // [B, Lq, HI]
-  float* scores;         // [B, Lq, Lk]
+  float* scores;         // [B, Lq, out_ld] (unless filtering, below)
   int B, Lq, Lk, q_start, HI, dI;
   int n_qtiles, n_splits;  // filled by the launcher
+  // Key sampling: the kernel scores the keys s = key_stride * s' (s' = 0,
+  // 1, ...) and writes score s' of a row at scores[row * out_ld + s'].
+  // Plain scoring: key_stride 1, out_ld Lk.
+  int key_stride, out_ld;
+  // Filtering (thresh non-null): no scores are written.  The keys of row r
+  // whose order key is >= thresh[r] are written, in ascending index order, as
+  // (max(key, 1), index) to the cap_s slots of (row r, split) in
+  // cand_key / cand_idx ([B*Lq, n_splits, cap_s]); unused slots get (0, -1)
+  // and row_count[r * n_splits + split] the number found (possibly > cap_s).
+  // The prefill shape only (q_len >= 8).
+  const uint32_t* thresh;
+  uint32_t* cand_key;
+  int32_t* cand_idx;
+  int32_t* row_count;
+  int cap_s;
+  // Row subset (non-null): only query tiles holding a row r with
+  // only_rows[r] != 0 are scored.
+  const int32_t* only_rows;
 };
 
 struct TopkArgs {
@@ -24,8 +42,21 @@ struct TopkArgs {
   int B, Lq, Lk, q_start, k;
   // filled by the launcher for the two-stage path
   int nseg;
-  uint32_t* cand_key;   // [B*Lq, nseg, k]
-  int32_t* cand_idx;    // [B*Lq, nseg, k]
+  uint32_t* cand_key;   // [B*Lq, nseg, seg_cap]
+  int32_t* cand_idx;    // [B*Lq, nseg, seg_cap]
+  int seg_cap;          // candidate slots per segment (k for the two-stage path)
+  // Row subset (non-null): rows r with only_rows[r] == 0 are left untouched.
+  const int32_t* only_rows;
+};
+
+// Selection fused with the indexer for long rows (topk.hip + indexer.hip):
+// sizes of its buffers, decided from the problem alone.
+struct FusedPlan {
+  bool use;          // the fused path applies
+  int stride;        // key sampling stride S
+  int ls;            // sampled keys per row: ceil(longest row / S), <= 32768
+  int n_splits;      // key-range splits of the filtering indexer
+  int cap_s;         // candidate slots per (row, split)
 };
 
 struct AttnArgs {
@@ -111,6 +142,18 @@ inline hipError_t launch_kernel(const void* kernel, dim3 grid, dim3 block, size_
 }
 
 hipError_t launch_index_scores(const IndexArgs& a, hipStream_t stream);
+// Key-range splits launch_index_scores would use for `a` (any key_stride).
+int index_splits(const IndexArgs& a);
+FusedPlan fused_plan(int B, int Lq, int Lk, int q_start, int HI, int dI, int k);
+// Per-row thresholds of the fused selection from the sampled scores
+// [B*Lq, ls]: an order key t such that, judging from the sample, a little
+// more than k of the row's keys are >= t.
+hipError_t launch_fused_threshold(const float* sample, uint32_t* thresh, int B, int Lq, int Lk, int q_start,
+                                  int k, int stride, int ls, hipStream_t stream);
+// Exact top-k of each row from the filtering indexer's candidate slots;
+// rows whose candidates cannot be trusted (a split overflowed its slots, or
+// fewer than k were found) get flags[r] = 1 and are left for the plain path.
+hipError_t launch_fused_select(const TopkArgs& a, const int32_t* row_count, int32_t* flags, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k);
 hipError_t launch_sparse_mla_attn(const AttnArgs& a, hipStream_t stream);

@@ -29,12 +29,6 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0 ties with +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Wave-wide inclusive scans through DPP row shifts and row broadcasts (VALU
 // only; a shuffle would be an LDS-crossbar round trip per step).  `id` is the
 // identity of `op`; lane 63 ends up with the wave total.
@@ -196,6 +190,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs a) {
   uint32_t* ctrl = scan_sh + kWaves + 1;   // [0] digit, [1] count above
 
   const int row = blockIdx.x;
+  if (a.only_rows && !a.only_rows[row]) return;
   const int t = row % a.Lq;
   const int pos = a.q_start + t;
   const int n = min(pos + 1, a.Lk);
@@ -479,6 +474,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
   __shared__ uint32_t cand_k[kCap];
   __shared__ int32_t cand_i[kCap];
   const int row = blockIdx.x;
+  if (a.only_rows && !a.only_rows[row]) return;
   const int pos = a.q_start + row % a.Lq;
   const int n = min(pos + 1, a.Lk);
   int32_t* out = a.indices + (size_t)row * a.k;
@@ -531,6 +527,7 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(TopkArgs a) {
   __shared__ int32_t cand_i[kCap];
   const int row = blockIdx.x / a.nseg;
   const int seg = blockIdx.x % a.nseg;
+  if (a.only_rows && !a.only_rows[row]) return;
   const int pos = a.q_start + row % a.Lq;
   const int n_row = min(pos + 1, a.Lk);
   if (n_row <= a.k) return;  // stage 2 writes short rows directly
@@ -558,9 +555,13 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(TopkArgs a) {
                           });
 }
 
-// Stage 2: one block per row selects among its nseg * k (<= 64 * NT) candidate slots.
+// Stage 2: one block per row selects among its nseg * seg_cap (<= 64 * NT)
+// candidate slots.  Fused selection (row_count non-null): the slots come from
+// the filtering indexer, and a row is selected only when every split kept all
+// its candidates within its slots and at least k were found; otherwise it is
+// flagged (flags[row] = 1) for the plain path.  Every row gets its flag.
 template <int NT>
-__global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a) {
+__global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t* row_count, int32_t* flags) {
   constexpr int EPT = 64;
   __shared__ uint32_t hist[kHist];
   __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
@@ -568,14 +569,34 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a) {
   __shared__ uint32_t cand_k[kCap];
   __shared__ int32_t cand_i[kCap];
   const int row = blockIdx.x;
+  if (a.only_rows && !a.only_rows[row]) return;
   const int pos = a.q_start + row % a.Lq;
   const int n_row = min(pos + 1, a.Lk);
   int32_t* out = a.indices + (size_t)row * a.k;
   if (n_row <= a.k) {
     for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < n_row ? i : -1;
+    if (flags && threadIdx.x == 0) flags[row] = 0;
     return;
   }
-  const int n = a.nseg * a.k;
+  if (row_count) {
+    if (threadIdx.x < 64) {
+      int found = 0, over = 0;
+      for (int sgi = threadIdx.x; sgi < a.nseg; sgi += 64) {
+        const int c = row_count[(size_t)row * a.nseg + sgi];
+        found += c;
+        over |= c > a.seg_cap;
+      }
+      found = (int)wave_scan_add((uint32_t)found);
+      over = __ballot(over) != 0;
+      if (threadIdx.x == 63) ctrl[3] = (over || found < a.k) ? 1u : 0u;
+    }
+    __syncthreads();
+    const bool bad = ctrl[3] != 0;
+    __syncthreads();
+    if (threadIdx.x == 0) flags[row] = bad ? 1 : 0;
+    if (bad) return;
+  }
+  const int n = a.nseg * a.seg_cap;
   const uint32_t* ck = a.cand_key + (size_t)row * n;
   const int32_t* ci = a.cand_idx + (size_t)row * n;
   const int base = EPT * threadIdx.x;
@@ -618,6 +639,41 @@ SegPlan topk_plan(long long rows, int Lq, int q_start, int Lk, int k) {
   return {0, false};
 }
 
+// Threshold of the fused selection for one row (one block per row): over
+// the row's sampled scores (keys s = stride * s'), an order key t with at
+// least r samples >= t, r a few standard deviations above the sampled rank
+// of the row's k-th largest key (as in select_top's own sample).  About
+// r * stride of the row's keys are then >= t, at least k of them with
+// overwhelming probability; the select kernel checks that.
+template <int EPT, int NT>
+__global__ __launch_bounds__(NT) void fused_threshold_kernel(const float* sample, uint32_t* thresh, int Lq, int Lk,
+                                                             int q_start, int k, int stride, int ls) {
+  __shared__ uint32_t hist[kHist];
+  __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
+  __shared__ uint32_t ctrl[4];
+  const int row = blockIdx.x;
+  const int pos = q_start + row % Lq;
+  const int n = min(pos + 1, Lk);
+  if (n <= k) {
+    if (threadIdx.x == 0) thresh[row] = 0u;
+    return;
+  }
+  const int m = min(pos / stride + 1, ls);  // sampled keys s' with stride * s' <= pos
+  // only counts matter here, so a thread holds the samples j * NT + tid
+  // (coalesced loads); those below m are a prefix j < cnt of its slots
+  const int tid = threadIdx.x;
+  const int cnt = tid < m ? min(EPT, (m - tid + NT - 1) / NT) : 0;
+  const float* src = sample + (size_t)row * ls + tid;
+  uint32_t key[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) key[j] = j < cnt ? order_key(src[j * NT]) : 0u;
+  const float qm = (float)k * (float)m / (float)n;
+  const uint32_t r = min((uint32_t)m, (uint32_t)(qm + 4.0f * sqrtf(qm) + 8.0f));
+  BlockSelect<NT> sel{hist, scan_sh, ctrl};
+  const uint32_t t = sel.coarse_threshold(key, cnt, r);
+  if (threadIdx.x == 0) thresh[row] = t;
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k) {
@@ -638,6 +694,7 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
   const SegPlan plan = topk_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
   a.nseg = plan.nseg;
   if (a.nseg > 0 && a.workspace) {
+    a.seg_cap = a.k;
     a.cand_key = (uint32_t*)a.workspace;
     a.cand_idx = (int32_t*)(a.cand_key + (size_t)rows * a.nseg * a.k);
     const bool vec = a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0;
@@ -650,12 +707,69 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
       e = launch_kernel(vec ? (const void*)topk_seg_kernel<32, 256, true> : (const void*)topk_seg_kernel<32, 256, false>,
                         sgrid, dim3(256), 0, stream, a);
     if (e != hipSuccess) return e;
+    const int32_t* no_count = nullptr;
+    int32_t* no_flags = nullptr;
     if ((long long)a.nseg * a.k > kCandMax)
-      return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a);
-    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a);
+      return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a, no_count, no_flags);
+    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a, no_count, no_flags);
   }
   const size_t base = (size_t)(kBins + kWaves + 1 + 4) * sizeof(uint32_t);
   return launch_kernel((const void*)topk_kernel, grid, dim3(kThreads), base, stream, a);
+}
+
+FusedPlan fused_plan(int B, int Lq, int Lk, int q_start, int HI, int dI, int k) {
+  FusedPlan f{};
+  const int max_n = min(q_start + Lq, Lk);
+  // Only where the plain path would take the two-stage top-k (rows longer
+  // than one block's candidate capacity): up to that length the one-pass
+  // select reads the written scores faster than the sampling, threshold and
+  // filtering passes cost.  The filtering indexer runs the prefill shape.
+  if (Lq < 8 || max_n <= kCandMax || max_n <= 2 * k) return f;
+  f.stride = 16;
+  while ((long long)f.stride * 32768 < max_n) f.stride *= 2;  // a sampled row fits one block
+  f.ls = (max_n + f.stride - 1) / f.stride;  // sampled keys any row reaches (<= 32768)
+  IndexArgs a{};
+  a.B = B; a.Lq = Lq; a.Lk = Lk; a.q_start = q_start; a.HI = HI; a.dI = dI; a.key_stride = 1;
+  f.n_splits = index_splits(a);
+  // expected candidates of a long row: r * stride (the threshold kernel's r
+  // for the longest row), spread over the splits; twice that per split plus
+  // 64, rounded up to a power of two (at least 256).  The margin covers the
+  // threshold's coarseness: it is the lower edge of a digit bin, so up to a
+  // few times r samples can lie above it.
+  const float m = (float)((max_n - 1) / f.stride + 1);
+  const float qm = (float)k * m / (float)max_n;
+  const float expect = (qm + 4.0f * sqrtf(qm) + 8.0f) * (float)f.stride;
+  const float per_split = 2.0f * expect / (float)f.n_splits + 64.0f;
+  int cap = 256;
+  while (cap < per_split) cap *= 2;
+  f.cap_s = cap;
+  f.use = (long long)f.n_splits * cap <= kCandWide;
+  return f;
+}
+
+hipError_t launch_fused_threshold(const float* sample, uint32_t* thresh, int B, int Lq, int Lk, int q_start, int k,
+                                  int stride, int ls, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)B * Lq));
+  if (ls <= 2048)
+    return launch_kernel((const void*)fused_threshold_kernel<16, 128>, grid, dim3(128), 0, stream, sample, thresh,
+                         Lq, Lk, q_start, k, stride, ls);
+  if (ls <= 8192)
+    return launch_kernel((const void*)fused_threshold_kernel<32, 256>, grid, dim3(256), 0, stream, sample, thresh,
+                         Lq, Lk, q_start, k, stride, ls);
+  if (ls <= 32768)
+    return launch_kernel((const void*)fused_threshold_kernel<64, 512>, grid, dim3(512), 0, stream, sample, thresh,
+                         Lq, Lk, q_start, k, stride, ls);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused_select(const TopkArgs& a, const int32_t* row_count, int32_t* flags, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)a.B * a.Lq));
+  const long long n = (long long)a.nseg * a.seg_cap;
+  if (n <= kCandMax)
+    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a, row_count, flags);
+  if (n <= kCandWide)
+    return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a, row_count, flags);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace dsa

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert {"dsa_index_scores", "dsa_topk", "dsa_sparse_mla_attn", "dsa_sparse_mla_attn_ws", "dsa_masked_mha_attn",
+    assert {"dsa_index_scores", "dsa_topk", "dsa_index_topk", "dsa_sparse_mla_attn", "dsa_sparse_mla_attn_ws", "dsa_masked_mha_attn",
             "dsa_sparse_mla_attn_bwd", "dsa_forward", "dsa_workspace_size", "dsa_status_string", "dsa_last_error"} <= set(names)
     lib = ctypes.CDLL(dsa.LIB_PATH)
     for n in names:
@@ -70,6 +70,8 @@ def test_boundary_signatures():
                                            "float*", "float*", "void*", "size_t", "void*"]),
         "dsa_forward": ("int", [P, "const uint8_t*", "const uint8_t*", "const float*", "const uint16_t*",
                                 "const uint16_t*", "float*", "float*", "int32_t*", "void*", "size_t", "void*"]),
+        "dsa_index_topk": ("int", [P, "const uint8_t*", "const uint8_t*", "const float*", "int32_t*", "void*",
+                                   "size_t", "void*"]),
         "dsa_workspace_size": ("size_t", [P, "int"]),
         "dsa_status_string": ("const char*", ["int"]),
         "dsa_last_error": ("const char*", []),
@@ -275,3 +277,35 @@ def test_forward_noalloc_checks():
     assert s == -1 and "k_idx" in msg
     s, msg = _status(dsa.dsa_forward_noalloc, dec, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, indices=FAKE + 4, stream=0)
     assert s == -5 and "indices" in msg
+
+
+def test_index_topk_checks():
+    """dsa_index_topk: its workspace is the score matrix and the top-k scratch
+    (plus, for rows longer than 32768 keys in a multi-query problem, the
+    sampled scores and candidate slots of the sampled path); the argument
+    checks of the indexer and the top-k apply."""
+    for p in (GOOD, MLA, Problem(1, 32768, 32768, 0, 64, 128, 2048, 128, 512, 64),
+              Problem(64, 1, 131072, 131071, 64, 128, 2048, 128, 512, 64)):
+        scores = p.batch * p.q_len * p.kv_len * 4
+        topk = dsa.workspace_size(p, dsa.DSA_OP_TOPK)
+        r = lambda n: (n + 255) // 256 * 256
+        assert dsa.workspace_size(p, dsa.DSA_OP_INDEX_TOPK) == r(scores) + r(topk)
+    chunk = Problem(1, 8192, 131072, 122880, 64, 128, 2048, 128, 512, 64)
+    base = chunk.q_len * chunk.kv_len * 4 + dsa.workspace_size(chunk, dsa.DSA_OP_TOPK)
+    sample = chunk.q_len * (131072 // 16) * 4  # one key in 16 scored for the threshold
+    ws = dsa.workspace_size(chunk, dsa.DSA_OP_INDEX_TOPK)
+    assert ws >= base + sample + chunk.q_len * 2048 * 8 and ws % 256 == 0
+    assert dsa.workspace_size(chunk, dsa.DSA_OP_FORWARD) >= ws + chunk.q_len * 2048 * 4
+    s, msg = _status(dsa.dsa_index_topk, chunk, FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, stream=0)
+    assert s == -4 and str(ws) in msg, msg
+    s, msg = _status(dsa.dsa_index_topk, chunk, FAKE, FAKE, FAKE, FAKE, FAKE + 16, ws, stream=0)
+    assert s == -5 and "workspace" in msg, msg
+    s, msg = _status(dsa.dsa_index_topk, chunk, FAKE, FAKE, FAKE, None, FAKE, ws, stream=0)
+    assert s == -1 and "indices" in msg, msg
+    s, msg = _status(dsa.dsa_index_topk, chunk, FAKE + 8, FAKE, FAKE, FAKE, FAKE, ws, stream=0)
+    assert s == -5 and "q_idx" in msg, msg
+    s, _ = _status(dsa.dsa_index_topk, Problem(**{**GOOD.__dict__, "topk": 4096}), FAKE, FAKE, FAKE, FAKE,
+                   FAKE, 1 << 30, stream=0)
+    assert s == -3
+    with pytest.raises(DsaError):
+        dsa.workspace_size(Problem(**{**GOOD.__dict__, "idx_dim": 48}), dsa.DSA_OP_INDEX_TOPK)

@@ -330,6 +330,10 @@ def test_attention_invalid_entries_masked_chunks_and_empty_rows(dsa, shape):
     assert np.abs(l[fin] - ref_l[fin]).max() <= ATOL
 
 
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
 def test_attention_score_range_far_above_the_first_chunk(dsa):
     """Late selected tokens whose scores exceed every earlier one by far more
     than 2^32 in probability (a latent row that is a large multiple of the
@@ -353,6 +357,16 @@ def test_attention_score_range_far_above_the_first_chunk(dsa):
     q_d = dev(q)
     ref_o, ref_l = oracle.sparse_mla_attn(kv, q, idx, np.arange(B, dtype=np.int32), 512, wl.softmax_scale)
     assert ref_l[:, 5].min() > 100.0  # the big score dominates head 5
+    # The big token's value row is 8x a query row (|v| up to ~36), so the
+    # absolute error that the rounding of the probabilities to bf16 for the
+    # value product brings (relative 2^-9 each, 2^-8 allowed) grows with |v|:
+    # per element, 2^-8 * sum_s p_s |v_sd| + 1e-3, p the exact probabilities.
+    bound = np.empty_like(ref_o, dtype=np.float64)
+    for b_ in range(B):
+        sel = bf16_to_f64(kv[b_, idx[b_]])                      # [k, 576]
+        z = wl.softmax_scale * (bf16_to_f64(q[b_]) @ sel.T)      # [H, k]
+        pr = np.exp(z - ref_l[b_].astype(np.float64)[:, None])
+        bound[b_] = 2.0 ** -8 * (pr @ np.abs(sel[:, :512])) + 1e-3
     ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_SPARSE_MLA_ATTN)
     for use_ws in (False, True):
         out = torch.empty((B, 1, 128, 512), dtype=torch.float32, device="cuda")
@@ -363,7 +377,8 @@ def test_attention_score_range_far_above_the_first_chunk(dsa):
         torch.cuda.synchronize()
         o = out.cpu().numpy()[:, 0]
         l = lse.cpu().numpy()[:, 0]
-        err = np.abs(o - ref_o).max()
+        err = np.abs(o - ref_o)
         lerr = np.abs(l - ref_l).max()
-        log(f"[score range] split={use_ws}: max-abs {err:.2e}, lse {lerr:.2e} (lse up to {ref_l.max():.1f})")
-        assert err <= ATOL and lerr <= ATOL * max(1.0, float(np.abs(ref_l).max()) / 100.0)
+        log(f"[score range] split={use_ws}: max-abs {err.max():.2e}, worst error/bound {(err / bound).max():.3f}, "
+            f"lse {lerr:.2e} (lse up to {ref_l.max():.1f})")
+        assert (err <= bound).all() and lerr <= ATOL * max(1.0, float(np.abs(ref_l).max()) / 100.0)
