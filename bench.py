@@ -2,10 +2,14 @@
 
 One step = one pass of the whole path over the L=32K prefill workload (batch 1,
 32768 query tokens, k=2048, FP8 indexer 64 heads x 128, 128 query heads,
-576-wide bf16 latents): dsa_index_scores -> dsa_topk -> dsa_sparse_mla_attn,
-launched back to back on one stream (the same launches dsa_forward makes), with
-HIP events between the kernels for per-kernel durations.  Inputs are seeded,
-synthetic and resident in HBM before timing starts.
+576-wide bf16 latents): dsa_index_topk -> dsa_sparse_mla_attn, launched back
+to back on one stream (the launches dsa_forward makes), with HIP events
+around each call.  dsa_index_topk is the indexer followed by the top-k (for
+rows past 32K keys, the sampled path that writes only candidate keys).
+After the timed steps, dsa_index_scores and dsa_topk are timed on their own
+(a few calls, events between them) for the indexer's and the top-k's
+per-kernel figures.  Inputs are seeded, synthetic and resident in HBM before
+timing starts.  --workload picks another of the seeded workloads.
 
 Prints one JSON line: query tokens/s, per-kernel times and rooflines, and the
 CPU oracle timed on a bounded row sample of the same workload.
@@ -451,28 +455,31 @@ def main():
 
     attn_name = "sparse_mla_attn" if args.attn == "sparse" else "masked_mha_attn"
     names = ["index_scores", "topk", attn_name]
+    iws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_INDEX_TOPK)
+    iws = torch.empty(iws_bytes, dtype=torch.uint8, device=dev)
+    # the header's workspace rule: beyond the score matrix and the top-k
+    # scratch only when the sampled path is taken
+    r256 = lambda n: (n + 255) // 256 * 256
+    sampled = iws_bytes > r256(4 * B * Lq * Lk) + r256(ws_bytes)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
+        dsa.dsa_index_topk(prob, q_idx, k_idx, w, indices, iws, iws_bytes, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        dsa.dsa_topk(prob, scores, indices, ws, ws_bytes, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
         if args.attn == "sparse":
             dsa.dsa_sparse_mla_attn_ws(prob, q, kv, indices, out, lse, aws, aws_bytes, stream=stream)
         else:
             dsa.dsa_masked_mha_attn(prob, q, kv, indices, out, lse, stream=stream)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -480,6 +487,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    # the indexer and the top-k as separate calls, for their own figures
+    n_stage = max(1, min(args.steps, 10))
+    stage_idx = torch.empty_like(indices)
+    stage_events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_stage)]
+    for i in range(-1, n_stage):
+        ev = stage_events[i] if i >= 0 else None
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.dsa_topk(prob, scores, stage_idx, ws, ws_bytes, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+    torch.cuda.synchronize()
+    del stage_idx
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -492,10 +516,14 @@ def main():
         print(f"[bench] calibration copies of {COPY_BYTES} bytes done", file=sys.stderr, flush=True)
 
     per = {n: [] for n in names}
+    per["index_topk"] = []
     for ev in events:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]))
-    step_ms = [ev[0].elapsed_time(ev[3]) for ev in events]
+        per["index_topk"].append(ev[0].elapsed_time(ev[1]))
+        per[attn_name].append(ev[1].elapsed_time(ev[2]))
+    for ev in stage_events:
+        per["index_scores"].append(ev[0].elapsed_time(ev[1]))
+        per["topk"].append(ev[1].elapsed_time(ev[2]))
+    step_ms = [ev[0].elapsed_time(ev[2]) for ev in events]
     ms_per_step = wall * 1e3 / args.steps
 
     work = algorithmic(wl)
@@ -514,6 +542,14 @@ def main():
         k.update(algorithmic_gbs=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS)
         kernels[n] = k
 
+    # the step's selection call: the indexer's roofline, plus the top-k's
+    # score read when the scores are written out
+    sel_roof = kernels["index_scores"]["roofline_ms"] + (0.0 if sampled else kernels["topk"]["roofline_ms"])
+    kernels["index_topk"] = {"avg_ms": float(np.mean(per["index_topk"])),
+                             "median_ms": float(np.median(per["index_topk"])),
+                             "min_ms": float(np.min(per["index_topk"])), "sampled_path": sampled,
+                             "roofline_ms": sel_roof, "stage_calls_timed": n_stage}
+
     dom = max(names, key=lambda n: kernels[n]["avg_ms"])
     kd = kernels[dom]
     if work[dom]["flop"]:
@@ -526,7 +562,7 @@ def main():
     roof["traffic"] = kd["hbm_bytes_per_launch"]
 
     value = wl.batch * wl.q_len * args.steps / wall
-    ceiling_ms = sum(kernels[n]["roofline_ms"] for n in names)
+    ceiling_ms = sel_roof + kernels[attn_name]["roofline_ms"]
     result = {
         "metric": metric_name(wl),
         "value": value,
@@ -549,6 +585,7 @@ def main():
         "roofline": roof,
         # the whole step against the sum of its kernels' roofline times
         "end_to_end": {"ceiling_ms": ceiling_ms, "ms_per_step": ms_per_step, "frac": ceiling_ms / ms_per_step,
+                       "sampled_selection": sampled,
                        "ceiling_query_tokens_per_s": wl.batch * wl.q_len / (ceiling_ms * 1e-3)},
         "indexer_fp8_tflops": kernels["index_scores"]["tflops"],
         "indexer_frac_of_fp8_peak": kernels["index_scores"]["frac_of_mfma_peak"],
@@ -556,7 +593,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        del scores, indices, out, lse, q, q_idx
+        del scores, indices, out, lse, q, q_idx, iws
         torch.cuda.empty_cache()
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -64,11 +64,17 @@ constexpr int kKeysPerWave = 64;
 // starts at +0.
 __device__ __forceinline__ float relu(float x) { return fmaxf(x, 0.0f); }
 
-// FILTER: instead of the scores, write the candidates above the row's
-// threshold (IndexArgs, "Filtering"); the prefill shape (one query per wave).
-template <int NKL, int NHG, bool FULLD, int NW, int kQPW, bool FILTER>
+// MODE 0: every key, scores written at [row, key].  MODE 1 (sampling): the
+// keys key_stride * s', scores at [row * out_ld + s'].  MODE 2 (filtering):
+// every key, and instead of the scores the candidates at or above the row's
+// threshold (IndexArgs, "Filtering").  Modes 1 and 2 run the prefill shape
+// (one query per wave); the stride is a compile-time 1 outside mode 1, so the
+// plain kernel's address arithmetic stays as simple as it can be.
+template <int NKL, int NHG, bool FULLD, int NW, int kQPW, int MODE>
 __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
-  static_assert(!FILTER || (NKL == 1 && kQPW == 1), "filtering runs one query per wave");
+  constexpr bool FILTER = MODE == 2;
+  constexpr bool SAMPLED = MODE == 1;
+  static_assert(MODE == 0 || (NKL == 1 && kQPW == 1), "sampling and filtering run one query per wave");
   constexpr int kThreads = 64 * NW;
   constexpr int NQG = NW / NKL;         // query groups per block
   constexpr int QT = kQPW * NQG;        // queries per block
@@ -95,7 +101,8 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
     if (!any) return;
   }
   // keys are s = stride * s' for s' < ls; a tile needs s' <= (its last position) / stride
-  const int stride = a.key_stride;
+  const int stride = SAMPLED ? a.key_stride : 1;
+  const int out_ld = SAMPLED ? a.out_ld : a.Lk;
   const int ls = (a.Lk + stride - 1) / stride;
   const int kv_end = min(ls, (a.q_start + t_last) / stride + 1);
   const int nst_total = (kv_end + KS - 1) / KS;
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(64 * NW) void index_scores_kernel(IndexArgs a) {
           cursor += __builtin_popcountll(m);
         }
       } else if (valid) {
-        a.scores[((size_t)b * a.Lq + t) * a.out_ld + key] = fin;
+        a.scores[((size_t)b * a.Lq + t) * out_ld + key] = fin;
       }
     }
 
@@ -359,7 +366,9 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
   IndexArgs a = args_in;
   const bool decode = a.Lq < 8;
   const bool filter = a.thresh != nullptr;
-  if (filter && decode) return hipErrorInvalidValue;
+  const bool sampled = a.key_stride != 1;
+  if ((filter || sampled) && decode) return hipErrorInvalidValue;
+  if (filter && sampled) return hipErrorInvalidValue;
   const int QT = decode ? kDecodeQPW * kDecodeWaves / 4 : kPrefillQPW * kPrefillWaves;
   const int KS = decode ? 4 * kKeysPerWave : kKeysPerWave;
   a.n_qtiles = (a.Lq + QT - 1) / QT;
@@ -376,19 +385,24 @@ hipError_t launch_index_scores(const IndexArgs& args_in, hipStream_t stream) {
   int threads;
   if (decode) {
     threads = 64 * kDecodeWaves;
-    kern = nhg == 1   ? DSA_K1(4, 1, kDecodeWaves, kDecodeQPW, false)
-           : nhg == 2 ? DSA_K1(4, 2, kDecodeWaves, kDecodeQPW, false)
-                      : DSA_K1(4, 4, kDecodeWaves, kDecodeQPW, false);
+    kern = nhg == 1   ? DSA_K1(4, 1, kDecodeWaves, kDecodeQPW, 0)
+           : nhg == 2 ? DSA_K1(4, 2, kDecodeWaves, kDecodeQPW, 0)
+                      : DSA_K1(4, 4, kDecodeWaves, kDecodeQPW, 0);
   } else if (filter) {
     threads = 64 * kPrefillWaves;
-    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, true)
-           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, true)
-                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, true);
+    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, 2)
+           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, 2)
+                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, 2);
+  } else if (sampled) {
+    threads = 64 * kPrefillWaves;
+    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, 1)
+           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, 1)
+                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, 1);
   } else {
     threads = 64 * kPrefillWaves;
-    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, false)
-           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, false)
-                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, false);
+    kern = nhg == 1   ? DSA_K1(1, 1, kPrefillWaves, kPrefillQPW, 0)
+           : nhg == 2 ? DSA_K1(1, 2, kPrefillWaves, kPrefillQPW, 0)
+                      : DSA_K1(1, 4, kPrefillWaves, kPrefillQPW, 0);
   }
 #undef DSA_K1
   if (smem > 64 * 1024) {

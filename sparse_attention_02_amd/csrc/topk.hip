@@ -726,7 +726,9 @@ FusedPlan fused_plan(int B, int Lq, int Lk, int q_start, int HI, int dI, int k) 
   // filtering passes cost.  The filtering indexer runs the prefill shape.
   if (Lq < 8 || max_n <= kCandMax || max_n <= 2 * k) return f;
   f.stride = 16;
-  while ((long long)f.stride * 32768 < max_n) f.stride *= 2;  // a sampled row fits one block
+  // at most 16384 sampled keys per row: the sampled pass and the threshold
+  // cost little next to the filtering pass (up to 32768 fit one block)
+  while ((long long)f.stride * 16384 < max_n) f.stride *= 2;
   f.ls = (max_n + f.stride - 1) / f.stride;  // sampled keys any row reaches (<= 32768)
   IndexArgs a{};
   a.B = B; a.Lq = Lq; a.Lk = Lk; a.q_start = q_start; a.HI = HI; a.dI = dI; a.key_stride = 1;
