@@ -12,27 +12,31 @@
 //
 // Mapping (one block of NW waves per query row):
 //  * Gather: the selected latent rows are copied 32 at a time straight into
-//    LDS with global_load_lds (no register staging), three chunks in flight.
-//    Rows are stored with their 16-byte pieces XOR-swizzled by (row & 7) so the
-//    operand reads below are free of LDS bank conflicts.
-//  * Scores: wave w owns 16*HTQ heads.  S^T[key, head] = K . Q^T on bf16 MFMA
-//    16x16x32 with Q^T resident in registers.
+//    LDS with global_load_lds (no register staging), up to three chunks in
+//    flight ahead of the one computed, by the older wave of each SIMD at the
+//    end of its chunk (see the gather below).  Rows are stored with their
+//    16-byte pieces XOR-swizzled by (row & 7) so the operand reads below are
+//    free of LDS bank conflicts.
+//  * Each wave owns 16*HTQ heads from scores to output, so the waves share
+//    nothing but the latent chunks and meet at one barrier per chunk.
+//  * Scores: S^T[key, head] = K . Q^T on bf16 MFMA 16x16x32 with Q^T resident
+//    in registers.
 //  * Softmax: fp32 in the exp2 domain with a lazily moved running maximum (the
 //    accumulators are only rescaled when a head's maximum grows by more than
-//    2^8, so probabilities stay <= 256).  P is rounded to bf16 and exchanged
-//    through LDS together with the per-head rescale factors.
-//  * Values: wave w owns output columns [DV/NW * w, DV/NW * (w+1)) for all 128
-//    heads: O^T[d, head] += V^T . P^T on bf16 MFMA 16x16x32.  V^T comes from the
-//    row-major latent chunk through the transposing ds_read_b64_tr_b16 and is
-//    reused by all eight 16-head tiles, so the slower transposing reads are
-//    issued once per wave and d-tile, not once per head tile.
-// Per SIMD, Q (128 heads) and the fp32 output accumulators (128 x 512) take
-// about 400 of the 512 registers whatever the split; NW = 8 runs two waves per
-// SIMD so one wave's softmax overlaps the other's matrix work.
-// The MFMA result layout of S^T leaves a lane with one head and the 8 keys
-// {4g..4g+3, 16+4g..16+4g+3} (g = lane/16); those 8 values are written as one
-// 16-byte row segment of P, and the V^T operand of lane group g reads exactly
-// those 8 latent rows, so both operands agree on the key order.
+//    2^8, so probabilities stay <= 256).  P is rounded to bf16 and stays in
+//    registers: the MFMA result layout of S^T leaves a lane with one head and
+//    the 8 keys {4g..4g+3, 16+4g..16+4g+3} (g = lane/16), which is exactly
+//    the B operand of the value product whose V^T operand (lane group g)
+//    reads those 8 latent rows.
+//  * Values: O^T[d, head] += V^T . P^T on bf16 MFMA 16x16x32 over all D_v
+//    columns of the wave's heads; V^T comes from the row-major latent chunk
+//    through the transposing ds_read_b64_tr_b16.
+// Per wave, Q^T (16 heads x 576) takes 72 registers and the fp32 output
+// accumulators (16 heads x 512) 128; NW = 8 runs two waves per SIMD, and with
+// no barrier between a wave's softmax and its value products one wave's
+// softmax overlaps the other's matrix work.  Every wave reads the whole chunk
+// (K for its scores, V for its values): 8 x 68 KiB of LDS reads per 32-key
+// chunk, against 8 x 68 matrix products of 16 x 16 x 32.
 #include "dsa_common.h"
 #include "launch.h"
 
@@ -41,27 +45,23 @@ namespace dsa {
 namespace {
 
 constexpr int kChunk = 32;     // keys per chunk
-constexpr int kStages = 3;     // latent chunks in flight
-constexpr int kHeadTiles = 8;  // 128 heads / 16
-constexpr int kPRow = 64;      // bytes of one head's P values (32 bf16)
 constexpr float kLazyMax = 8.0f;
 
 template <int DQK, int DV, int NW>
 struct AttnShape {
   static constexpr int DQKP = (DQK + 31) / 32 * 32;  // score width padded to K=32 steps
   static constexpr int KST = DQKP / 32;
-  static constexpr int HTQ = 128 / 16 / NW;         // 16-head score tiles per wave
-  static constexpr int DTW = DV / 16 / NW;          // value d-tiles per wave
+  static constexpr int HTQ = 128 / 16 / NW;         // 16-head tiles per wave
+  static constexpr int DT = DV / 16;                // value d-tiles (all of them, per wave)
   static constexpr int RS = DQKP * 2;               // LDS bytes per latent row
   static constexpr int PPR = RS / 16;               // 16-byte pieces per LDS row
   static constexpr int RPR = DQK * 2 / 16;          // pieces present in the cache row
   static constexpr int CHUNK_BYTES = kChunk * RS;
   static constexpr int DMA_BLOCKS = CHUNK_BYTES / 1024;  // 64 lanes x 16 bytes
   static constexpr bool SWZ = PPR % 8 == 0;
-  static constexpr int P_BYTES = 128 * kPRow;
   static_assert(CHUNK_BYTES % 1024 == 0, "chunk must be whole 1 KiB DMA blocks");
   static_assert(HTQ >= 1 && HTQ * 16 * NW == 128, "score heads must tile 128");
-  static_assert(DQK % 8 == 0 && DTW >= 1 && DTW * 16 * NW == DV && DV <= DQK, "unsupported latent shape");
+  static_assert(DQK % 8 == 0 && DV % 16 == 0 && DV <= DQK, "unsupported latent shape");
 };
 
 // q / d for 0 <= q < n as (q * ceil(2^19 / d)) >> 19: exact when every q in
@@ -127,15 +127,14 @@ __device__ __forceinline__ void wait_vmcnt() {
 // MASKED: the masked mode for short prefill.  The row's whole causal range
 // [0, pos(t)] is streamed in contiguous chunks and the entries outside the
 // selection are masked in the softmax, instead of gathering the selected rows.
-template <int DQK, int DV, int NW, bool MASKED>
+// STAGES: latent chunks in the LDS ring (STAGES - 1 gathers in flight).
+template <int DQK, int DV, int NW, bool MASKED, int STAGES>
 __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   using S = AttnShape<DQK, DV, NW>;
+  static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 chunk buffers");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* kvb = smem;                                        // [kStages][CHUNK_BYTES]
-  uint8_t* pbuf = smem + kStages * S::CHUNK_BYTES;            // [2][8 tiles][4 g][16 heads][16 B]
-  float* alpha_s = (float*)(pbuf + 2 * S::P_BYTES);           // [2][16 lanes][8 head tiles]
-  float* lsum_s = alpha_s + 2 * 128;                          // [128]
-  int32_t* sidx = (int32_t*)(lsum_s + 128);                   // [nch * kChunk]
+  uint8_t* kvb = smem;                                        // [STAGES][CHUNK_BYTES]
+  int32_t* sidx = (int32_t*)(smem + STAGES * S::CHUNK_BYTES);  // [nch * kChunk]
   uint32_t* selm = (uint32_t*)sidx;  // masked mode: [nch] selection bit per key of a chunk
 
   const int lane = threadIdx.x & 63;
@@ -164,10 +163,6 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   const int nch = ((MASKED ? n_keys : a.k) + kChunk - 1) / kChunk;
   // chunks [c_lo, c_hi) of the row belong to this block
   const int c_lo = part * nch / a.nsplit, c_hi = (part + 1) * nch / a.nsplit;
-  float* out_base = a.nsplit > 1 ? a.part_out + (size_t)vb * a.H * DV
-                                 : a.out + (size_t)row * a.H * DV;
-  float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)vb * a.H
-                                 : (a.lse ? a.lse + (size_t)row * a.H : nullptr);
 
   uint64_t chunk_mask = 0, full_mask = 0;  // sparse: chunks with some / with only valid entries
   const int32_t* idx_row = a.indices + (size_t)row * a.k;
@@ -201,7 +196,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     full_mask = __ballot(all);
   }
 
-  // ---- Q^T fragments of this wave's score heads (B operand)
+  // ---- Q^T fragments of this wave's heads (B operand of the score products)
   v8bf qf[S::HTQ][S::KST];
 #pragma unroll
   for (int ht = 0; ht < S::HTQ; ++ht) {
@@ -218,30 +213,37 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     }
   }
 
-  // ---- gather of one chunk: this wave copies the 1 KiB blocks [j_lo, j_lo + n_j)
-  // of the chunk (4 or 5 for the 576-wide rows), so one M0 value (the LDS
-  // address of block j_lo + 2) and immediate offsets -2048..2048 reach them all.
-  // The global base sits 4 KiB below the sequence's cache so that the per-lane
-  // offsets, which absorb the immediate, stay non-negative.
+  // ---- gather of one chunk by the first GW waves, BPW 1 KiB blocks each
+  // (blocks [BPW*w, BPW*w + BPW)), in runs of up to 5 blocks: one M0 value
+  // per run (the LDS address of the run's third block) and immediate offsets
+  // -2048..2048 reach a run's blocks.  Waves w and w + NW/2 share a SIMD and
+  // the older one (w < NW/2) is issued first, so it reaches the end of a
+  // chunk first; it takes the whole copy while the younger wave catches up.
+  // The global base sits 4 KiB below the sequence's cache so that the
+  // per-lane offsets, which absorb the immediate, stay non-negative.
   const uint8_t* kv_bias = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK) - 4096;
-  constexpr int NJ = (S::DMA_BLOCKS + NW - 1) / NW;
-  static_assert(NJ <= 5 && S::DMA_BLOCKS / NW >= 1, "1 to 5 copies per wave and chunk");
+  constexpr int GW = NW / 2;
+  constexpr int BPW = S::DMA_BLOCKS / GW;
+  constexpr int R1 = BPW < 5 ? BPW : 5;  // blocks of the first run
+  constexpr int R2 = BPW - R1;            // and of the second
+  static_assert(S::DMA_BLOCKS % GW == 0 && R2 <= 5, "whole runs of 1 to 5 blocks per gathering wave");
   static_assert(div_mul_exact(S::PPR, 64 * S::DMA_BLOCKS), "piece -> row split by multiply-shift");
-  const int j_lo = wave * S::DMA_BLOCKS / NW;
-  const bool long_run = (wave + 1) * S::DMA_BLOCKS / NW - j_lo == NJ;
+  const bool gathers = wave < GW;
+  const int j_lo = wave * BPW;
   auto issue = [&](int c, int buf) {
+    if (!gathers) return;
     // All row indices are read before the copies are issued: the copies are
-    // one asm statement with a memory clobber, so no look-up can move past it.
+    // asm statements with a memory clobber, so no look-up can move past them.
     // The lane offsets are recomputed per call (hoisting them out of the chunk
-    // loop would hold ~10 registers), and any spill reload here would make the
+    // loop would hold BPW registers), and any spill reload here would make the
     // compiler wait for every gather in flight.
     int ln;
     asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
-    uint32_t off[5] = {0, 0, 0, 0, 0};
+    uint32_t off[2][5] = {{0, 0, 0, 0, 0}, {0, 0, 0, 0, 0}};
 #pragma unroll
-    for (int j0 = 0; j0 < NJ; ++j0) {
-      const int j = min(j_lo + j0, S::DMA_BLOCKS - 1);
-      const uint32_t p = 64u * (uint32_t)j + (uint32_t)ln;
+    for (int j1 = 0; j1 < BPW; ++j1) {
+      const int run = j1 < R1 ? 0 : 1, j0 = j1 < R1 ? j1 : j1 - R1;
+      const uint32_t p = 64u * (uint32_t)(j_lo + j1) + (uint32_t)ln;
       const uint32_t r = __umul24(p, div_mul(S::PPR)) >> kDivShift;
       const uint32_t pp = p - r * (uint32_t)S::PPR;
       const uint32_t lp = S::SWZ ? (pp ^ (r & 7u)) : pp;
@@ -252,22 +254,30 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       if constexpr (S::PPR != S::RPR) src_col = lp < (uint32_t)S::RPR ? lp : lp - S::RPR;
       const int idx = MASKED ? min(kChunk * c + (int)r, n_keys - 1) : max(sidx[c * kChunk + r], 0);
       // row indices are < 2^24 and the cache is < 4 GiB - 8 KiB (checked by the host)
-      off[j0] = __umul24((uint32_t)idx, DQK * 2) + 16 * src_col + 4096 - 1024 * (j0 - 2);
+      off[run][j0] = __umul24((uint32_t)idx, DQK * 2) + 16 * src_col + 4096 - 1024 * (j0 - 2);
     }
-    const uint32_t mid =
-        __builtin_amdgcn_readfirstlane(lds_offset(kvb + buf * S::CHUNK_BYTES + 1024 * (j_lo + 2)));
-    if (long_run) dma_run<NJ>(mid, kv_bias, off);
-    else dma_run<NJ - 1>(mid, kv_bias, off);
+    const uint8_t* dst = kvb + buf * S::CHUNK_BYTES + 1024 * j_lo;
+    dma_run<R1>(__builtin_amdgcn_readfirstlane(lds_offset(dst + 1024 * 2)), kv_bias, off[0]);
+    if constexpr (R2 > 0)
+      dma_run<R2>(__builtin_amdgcn_readfirstlane(lds_offset(dst + 1024 * (R1 + 2))), kv_bias, off[1]);
+  };
+  // wait until this wave's copies of all but the `later` (0 .. STAGES - 2)
+  // most recently issued chunks have landed
+  auto wait_gather = [&](int later) {
+    if (!gathers) return;
+    if (later <= 0) wait_vmcnt<0>();
+    else if (later == 1 || STAGES < 4) wait_vmcnt<BPW>();
+    else wait_vmcnt<2 * BPW>();
   };
 
   // physical byte offset of logical 16-byte piece `lp` in LDS row `r`
   auto piece = [](int r, int lp) { return 16 * (S::SWZ ? (lp ^ (r & 7)) : lp); };
 
-  v4f acc[kHeadTiles][S::DTW];
+  v4f acc[S::HTQ][S::DT];
 #pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht)
+  for (int ht = 0; ht < S::HTQ; ++ht)
 #pragma unroll
-    for (int dt = 0; dt < S::DTW; ++dt) acc[ht][dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int dt = 0; dt < S::DT; ++dt) acc[ht][dt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   float m_use[S::HTQ], l_part[S::HTQ];
 #pragma unroll
   for (int ht = 0; ht < S::HTQ; ++ht) {
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     }
   };
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue_next(s);
+  for (int s = 0; s < STAGES - 1; ++s) issue_next(s);
 
   // Per-lane LDS byte offsets of the operand reads.  With the swizzle, logical
   // piece lp of row r sits at piece lp ^ (r & 7): 8*(lp>>3) + ((lp&7) ^ (r&7)).
@@ -300,18 +310,18 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
 #pragma unroll
   for (int par = 0; par < 2; ++par) k_off[par] = li * S::RS + piece(li, 4 * par + g);
   //  V^T rows 4g + li/4 (k-slots 8g..8g+3) and 16 + 4g + li/4 (8g+4..8g+7),
-  //  both with row & 7 == (4g + li/4) & 7; logical piece 2*dtg + (li&3)/2 of
-  //  d-tile dtg, plus 8*(li&1) bytes inside the piece.
+  //  both with row & 7 == (4g + li/4) & 7; logical piece 2*dt + (li&3)/2 of
+  //  d-tile dt, plus 8*(li&1) bytes inside the piece.
+  //  Pieces 2dt + sel and 2(dt + 4) + sel differ by 8, outside the swizzle's
+  //  low 3 bits, so four per-lane bases (dt & 3) plus a compile-time 128-byte
+  //  step per 4 d-tiles reach every d-tile.
   const int r_v0 = 4 * g + (li >> 2);
-  const int v_base = r_v0 * S::RS + 8 * (li & 1);
-  const int v_sel = (li & 3) >> 1;
-  //  P is stored piece-major: the 16-byte piece g of head 16ht + li sits at
-  //  1024 ht + 256 g + 16 li, so both its writes and its reads are linear in
-  //  the lane index.  (A head-major layout with an XOR swizzle, balanced over
-  //  the 64 banks on paper, measured at half the LDS read rate.)
-  const int p_off = 256 * g + 16 * li;
+  int v_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v_off[q] = r_v0 * S::RS + 8 * (li & 1) + piece(r_v0, 2 * q + ((li & 3) >> 1));
 
-  for (int it = 0; it < total; ++it) {
+  int buf = 0;  // it % STAGES
+  for (int it = 0; it < total; ++it, buf = buf + 1 == STAGES ? 0 : buf + 1) {
     int c;
     if constexpr (MASKED) {
       c = c_lo + it;
@@ -319,17 +329,12 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       c = __builtin_ctzll(to_compute);
       to_compute &= to_compute - 1;
     }
-    const int buf = it % kStages;
     const uint8_t* kb = kvb + buf * S::CHUNK_BYTES;
-    const int pslot = it & 1;
 
-    // wait for this chunk's gather: at most one later chunk is in flight here
-    if (it + 1 < total) {
-      if (long_run) wait_vmcnt<NJ>();
-      else wait_vmcnt<NJ - 1>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // This chunk's rows have landed (for this wave's copies; the barrier then
+    // covers every wave's), and every wave is done with the previous chunk,
+    // whose buffer takes the next gather.
+    wait_gather(min(total - 1 - it, STAGES - 2));
     __syncthreads();
 
     // ---- S^T = K_chunk . Q^T for 2 key tiles x HTQ head tiles
@@ -338,39 +343,47 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     for (int ht = 0; ht < S::HTQ; ++ht)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) s[ht][kt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-    // K fragments are prefetched two K-steps ahead; the scheduling fences keep
-    // the compiler from hoisting the whole chunk's loads (register pressure).
-    constexpr int kPre = 2;
-    v8bf kf[kPre + 1][2];
-    auto load_k = [&](int ks, v8bf* dst) {
+    {
+      // K fragments are prefetched two K-steps ahead; the scheduling fences
+      // keep the compiler from hoisting the whole chunk's loads (registers).
+      constexpr int kPre = 2;
+      v8bf kf[kPre + 1][2];
+      auto load_k = [&](int ks, v8bf* dst) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-        dst[kt] = __builtin_bit_cast(
-            v8bf, *(const v4i*)(kb + k_off[ks & 1] + 16 * kt * S::RS + 128 * (ks >> 1)));
-    };
+        for (int kt = 0; kt < 2; ++kt)
+          dst[kt] = __builtin_bit_cast(
+              v8bf, *(const v4i*)(kb + k_off[ks & 1] + 16 * kt * S::RS + 128 * (ks >> 1)));
+      };
 #pragma unroll
-    for (int ks = 0; ks < kPre && ks < S::KST; ++ks) load_k(ks, kf[ks]);
+      for (int ks = 0; ks < kPre && ks < S::KST; ++ks) load_k(ks, kf[ks]);
 #pragma unroll
-    for (int ks = 0; ks < S::KST; ++ks) {
-      if (ks + kPre < S::KST) load_k(ks + kPre, kf[(ks + kPre) % (kPre + 1)]);
+      for (int ks = 0; ks < S::KST; ++ks) {
+        if (ks + kPre < S::KST) load_k(ks + kPre, kf[(ks + kPre) % (kPre + 1)]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int ht = 0; ht < S::HTQ; ++ht)
-          s[ht][kt] = mfma_bf16_16x16x32(kf[ks % (kPre + 1)][kt], qf[ht][ks], s[ht][kt]);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int ht = 0; ht < S::HTQ; ++ht)
+            s[ht][kt] = mfma_bf16_16x16x32(kf[ks % (kPre + 1)][kt], qf[ht][ks], s[ht][kt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
-    // ---- softmax for this lane's heads over its 8 keys; P and alpha -> LDS
+    // ---- softmax for this lane's heads over its 8 keys, in registers
     // Raw scores; the scale (> 0, so it keeps the order) is applied to the
     // maximum and folded into the exponent's FMA.  Only chunks holding
     // invalid entries (-1 padding) are masked: a wave-uniform branch.  In
     // masked mode chunks not wholly selected are masked by their bits; a head's
     // maximum stays -inf until a selected entry is seen, and while it does
     // every score is -inf and is taken against 0 (giving p = 0, not NaN).
+    // P leaves as bf16 in exactly the B-operand layout of the value products:
+    // the lane holds head li and keys {4g..4g+3, 16+4g..16+4g+3}, the k-slots
+    // 8g..8g+7 of the transposed latent rows read below.
     uint32_t bits = 0;
     if constexpr (MASKED) bits = __builtin_amdgcn_readfirstlane(selm[c]);
     const bool full = MASKED ? bits == 0xFFFFFFFFu : (full_mask >> c) & 1;
+    v8bf pf[S::HTQ];
+    float al[S::HTQ];
+    bool rescale = false;
 #pragma unroll
     for (int ht = 0; ht < S::HTQ; ++ht) {
       float z[8];
@@ -397,10 +410,11 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       float mloc = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])),
                          fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
       mloc = max_xor32(max_xor16(mloc)) * a.scale_log2;
-      float al = 1.0f;
+      al[ht] = 1.0f;
       if (mloc > m_use[ht] + kLazyMax) {
-        al = fast_exp2(m_use[ht] - mloc);
+        al[ht] = fast_exp2(m_use[ht] - mloc);
         m_use[ht] = mloc;
+        rescale = true;
       }
       uint32_t pk[4];
       float psum = 0.0f;
@@ -413,86 +427,59 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
         psum += p0 + p1;
         pk[i] = pack_bf16x2(p0, p1);
       }
-      l_part[ht] = l_part[ht] * al + psum;
-      const int head = 16 * (S::HTQ * wave + ht) + li;
-      *(v4i*)(pbuf + pslot * S::P_BYTES + 1024 * (head >> 4) + p_off) =
-          (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-      if (g == 0) alpha_s[pslot * 128 + li * kHeadTiles + (head >> 4)] = al;
+      l_part[ht] = l_part[ht] * al[ht] + psum;
+      pf[ht] = __builtin_bit_cast(v8bf, (v4i){(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]});
     }
-    __syncthreads();
-
-    // the chunk before this one is done everywhere: reuse its buffer for the next gather
-    issue_next((it + kStages - 1) % kStages);
-
-    // ---- O^T = alpha * O^T + V^T . P^T for this wave's d-range, all 128 heads
-    float al8[kHeadTiles];
-    {
-      const v4f a0 = *(const v4f*)(alpha_s + pslot * 128 + li * kHeadTiles);
-      const v4f a1 = *(const v4f*)(alpha_s + pslot * 128 + li * kHeadTiles + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        al8[i] = a0[i];
-        al8[4 + i] = a1[i];
-      }
-    }
-    bool rescale = false;
-#pragma unroll
-    for (int ht = 0; ht < kHeadTiles; ++ht) rescale |= al8[ht] != 1.0f;
     if (__ballot(rescale)) {
 #pragma unroll
-      for (int ht = 0; ht < kHeadTiles; ++ht)
+      for (int ht = 0; ht < S::HTQ; ++ht)
 #pragma unroll
-        for (int dt = 0; dt < S::DTW; ++dt) acc[ht][dt] *= al8[ht];
+        for (int dt = 0; dt < S::DT; ++dt) acc[ht][dt] *= al[ht];
     }
-    // V^T fragments of this wave's d-tiles, then one P fragment per head tile
-    v8bf va[S::DTW];
-#pragma unroll
-    for (int dt = 0; dt < S::DTW; ++dt) {
-      const int voff = v_base + piece(r_v0, 2 * (wave * S::DTW + dt) + v_sel);
+
+    // ---- O^T = O^T + V^T . P^T for every d-tile of this wave's heads; V^T
+    // through the transposing reads, kVPre d-tiles ahead
+    constexpr int kVPre = S::DT < 2 ? S::DT : 2;
+    __builtin_amdgcn_sched_barrier(0);
+    v8bf va[kVPre];
+    auto load_v = [&](int dt) {
+      const int voff = v_off[dt & 3] + 128 * (dt >> 2);
       const v4s lo = lds_read_tr16(kb + voff);
       const v4s hi = lds_read_tr16(kb + voff + 16 * S::RS);
-      va[dt] = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-    }
-    const uint8_t* pb = pbuf + pslot * S::P_BYTES + p_off;
-    auto load_p = [&](int ht) { return __builtin_bit_cast(v8bf, *(const v4i*)(pb + 16 * kPRow * ht)); };
-    v8bf pf[2];
-    pf[0] = load_p(0);
+      return __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    };
 #pragma unroll
-    for (int ht = 0; ht < kHeadTiles; ++ht) {
-      if (ht + 1 < kHeadTiles) pf[(ht + 1) & 1] = load_p(ht + 1);
+    for (int dt = 0; dt < kVPre; ++dt) va[dt] = load_v(dt);
 #pragma unroll
-      for (int dt = 0; dt < S::DTW; ++dt) acc[ht][dt] = mfma_bf16_16x16x32(va[dt], pf[ht & 1], acc[ht][dt]);
+    for (int dt = 0; dt < S::DT; ++dt) {
+      const v8bf v = va[dt % kVPre];
+      if (dt + kVPre < S::DT) va[dt % kVPre] = load_v(dt + kVPre);
+#pragma unroll
+      for (int ht = 0; ht < S::HTQ; ++ht) acc[ht][dt] = mfma_bf16_16x16x32(v, pf[ht], acc[ht][dt]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // the next gather, into the buffer every wave released at this chunk's
+    // barrier; issued last so that the copies queue while waves wait there
+    issue_next(buf == 0 ? STAGES - 1 : buf - 1);
   }
 
-  // ---- row sums of the score heads -> LDS; lse
+  // ---- row sums, lse, and this wave's heads normalised and stored
+  float* out_base = a.nsplit > 1 ? a.part_out + (size_t)vb * a.H * DV
+                                 : a.out + (size_t)row * a.H * DV;
+  float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)vb * a.H
+                                 : (a.lse ? a.lse + (size_t)row * a.H : nullptr);
 #pragma unroll
   for (int ht = 0; ht < S::HTQ; ++ht) {
     float l = l_part[ht] + __shfl_xor(l_part[ht], 16);
     l += __shfl_xor(l, 32);
     const int head = 16 * (S::HTQ * wave + ht) + li;
-    if (g == 0) {
-      lsum_s[head] = l;
-      if (lse_base && head < a.H)
-        lse_base[head] = l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
-    }
-  }
-  __syncthreads();
-
-  // ---- normalise and store this wave's columns of every head
-#pragma unroll
-  for (int ht = 0; ht < kHeadTiles; ++ht) {
-    const int head = 16 * ht + li;
     if (head < a.H) {
-      const float l = lsum_s[head];
+      if (g == 0 && lse_base)
+        lse_base[head] = l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       float* orow = out_base + (size_t)head * DV;
 #pragma unroll
-      for (int dt = 0; dt < S::DTW; ++dt) {
-        const int d0 = 16 * (wave * S::DTW + dt) + 4 * g;
-        *(v4f*)(orow + d0) = acc[ht][dt] * inv;
-      }
+      for (int dt = 0; dt < S::DT; ++dt) *(v4f*)(orow + 16 * dt + 4 * g) = acc[ht][dt] * inv;
     }
   }
 }
@@ -523,22 +510,32 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
+template <int DQK, int DV, int NW, bool MASKED, int STAGES>
+hipError_t launch_stages(const AttnArgs& a, size_t smem, hipStream_t stream) {
+  const void* kern = (const void*)sparse_mla_kernel<DQK, DV, NW, MASKED, STAGES>;
+  static const hipError_t attr = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (attr != hipSuccess) return attr;
+  const long long rows = (long long)a.B * a.Lq;
+  return launch_kernel(kern, dim3((unsigned)(rows * a.nsplit)), dim3(64 * NW), smem, stream, a);
+}
+
 template <int DQK, int DV, int NW, bool MASKED>
 hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
   using S = AttnShape<DQK, DV, NW>;
   // sparse: the staged indices; masked: one selection word per chunk of the row
   const size_t tail = MASKED ? (size_t)((a.Lk + kChunk - 1) / kChunk) * sizeof(uint32_t)
                              : (size_t)((a.k + kChunk - 1) / kChunk) * kChunk * sizeof(int32_t);
-  const size_t smem = (size_t)kStages * S::CHUNK_BYTES + 2 * (size_t)S::P_BYTES +
-                      3 * 128 * sizeof(float) + tail;
-  static const hipError_t attr = hipFuncSetAttribute(
-      (const void*)sparse_mla_kernel<DQK, DV, NW, MASKED>, hipFuncAttributeMaxDynamicSharedMemorySize,
-      160 * 1024);
-  if (attr != hipSuccess) return attr;
-  const long long rows = (long long)a.B * a.Lq;
-  const hipError_t e = launch_kernel((const void*)sparse_mla_kernel<DQK, DV, NW, MASKED>,
-                                     dim3((unsigned)(rows * a.nsplit)), dim3(64 * NW), smem, stream, a);
+  // four chunk buffers where the LDS holds them, else three
+  constexpr size_t kLds = 160 * 1024;
+  hipError_t e;
+  if (4 * (size_t)S::CHUNK_BYTES + tail <= kLds)
+    e = launch_stages<DQK, DV, NW, MASKED, 4>(a, 4 * (size_t)S::CHUNK_BYTES + tail, stream);
+  else if (3 * (size_t)S::CHUNK_BYTES + tail <= kLds)
+    e = launch_stages<DQK, DV, NW, MASKED, 3>(a, 3 * (size_t)S::CHUNK_BYTES + tail, stream);
+  else
+    return hipErrorInvalidValue;
   if (e != hipSuccess || a.nsplit == 1) return e;
+  const long long rows = (long long)a.B * a.Lq;
   return launch_kernel((const void*)attn_combine_kernel, dim3((unsigned)(rows * a.H)), dim3(128), 0,
                        stream, a);
 }
