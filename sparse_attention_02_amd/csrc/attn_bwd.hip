@@ -38,6 +38,10 @@ namespace {
 constexpr int kBChunk = 32;   // keys per chunk
 constexpr int kBTiles = 8;    // 128 heads / 16 (absent heads are zero)
 constexpr int kBHeads = 128;  // padded head count of the key-major buffers
+// per head tile and chunk, the scores kernel stores one 16-byte dZ fragment
+// and one 2-byte P and dZ value for each of a lane's 8 keys
+constexpr int kScoreStoreKeys = 8;
+constexpr int kScoreStores = 1 + 2 * kScoreStoreKeys;
 
 template <int DQK, int DV, int NW>
 struct BwdShape {
@@ -75,6 +79,22 @@ __device__ __forceinline__ int opaque_tid() {
   int t;
   asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
   return t;
+}
+
+// Global stores issued through inline assembly, one instruction each, in
+// the loops whose vmcnt waits count them: the number of vector memory
+// operations between a chunk's copies and the wait is then fixed by the
+// source, not by how the compiler might split or merge the stores.  The
+// s_nop keeps the store data registers untouched for the wait states a
+// VALU write after a store needs (the hazard check does not see into asm).
+__device__ __forceinline__ void store_b128(void* p, v4i v) {
+  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_b64(void* p, v2i v) {
+  asm volatile("global_store_dwordx2 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void store_b16(void* p, uint32_t v) {
+  asm volatile("global_store_short %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -272,7 +292,7 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
     for (int ht = 0; ht < S::HTQ; ++ht) {
       const int tile = S::HTQ * wave + ht;
       const int head = 16 * tile + li;
-      float pv[8], zv[8];
+      float pv[kScoreStoreKeys], zv[kScoreStoreKeys];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -286,23 +306,24 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
       // dZ in the B-operand order of the dq kernel (k-slots 8g..8g+7)
       const v4i zf = {(int)pack_bf16x2(zv[0], zv[1]), (int)pack_bf16x2(zv[2], zv[3]),
                       (int)pack_bf16x2(zv[4], zv[5]), (int)pack_bf16x2(zv[6], zv[7])};
-      *(v4i*)(a.ws_dzf + ((((size_t)row * nch + c) * kBTiles + tile) * 64 + lane) * 8) = zf;
+      store_b128(a.ws_dzf + ((((size_t)row * nch + c) * kBTiles + tile) * 64 + lane) * 8, zf);
       // P and scale * dZ key-major [row][slot][128 heads] for the dkv products
       const int ln = opaque_tid() & 63;
       const size_t kmbase = ((size_t)row * kpad + (size_t)c * kBChunk + 4 * (ln >> 4)) * kBHeads +
                             16 * tile + (ln & 15);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < kScoreStoreKeys; ++e) {
         const size_t o = kmbase + (size_t)(16 * (e >> 2) + (e & 3)) * kBHeads;
-        a.ws_pk[o] = (uint16_t)(pack_bf16x2(pv[e], 0.0f) & 0xFFFFu);
-        a.ws_dzk[o] = (uint16_t)(pack_bf16x2(zv[e] * a.scale, 0.0f) & 0xFFFFu);
+        store_b16(a.ws_pk + o, pack_bf16x2(pv[e], 0.0f) & 0xFFFFu);
+        store_b16(a.ws_dzk + o, pack_bf16x2(zv[e] * a.scale, 0.0f) & 0xFFFFu);
       }
     }
     // the next chunk's copies are complete and every wave is done with this
     // one.  Vector memory operations retire in issue order, so waiting until
-    // only this chunk's stores (1 + 16 per head tile, issued after the copies)
-    // may be outstanding is enough: the stores drain behind the next chunk.
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(17 * S::HTQ) : "memory");
+    // only this chunk's stores (kScoreStores per head tile, all issued after
+    // the copies) may be outstanding is enough: the stores drain behind the
+    // next chunk.
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kScoreStores * S::HTQ) : "memory");
     __syncthreads();
   }
 }
@@ -649,13 +670,13 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkv_part_kernel(AttnBwdArgs 
       uint16_t* prow = a.ws_part + ((size_t)row * kpad + (size_t)c * kBChunk + 16 * kt + li) * DQK;
 #pragma unroll
       for (int j = 0; j < TPW; ++j)
-        *(v2i*)(prow + 16 * (wave + NW * j) + 4 * g) = (v2i){(int)pack_bf16x2(acc[j][kt][0], acc[j][kt][1]),
-                                                             (int)pack_bf16x2(acc[j][kt][2], acc[j][kt][3])};
+        store_b64(prow + 16 * (wave + NW * j) + 4 * g, (v2i){(int)pack_bf16x2(acc[j][kt][0], acc[j][kt][1]),
+                                                            (int)pack_bf16x2(acc[j][kt][2], acc[j][kt][3])});
     }
     // the next chunk's copies are complete and every wave is done with this
-    // one; only this chunk's 2 * TPW partial-row stores (issued after the
-    // copies; vector memory operations retire in issue order) may still be
-    // outstanding
+    // one; only this chunk's 2 * TPW partial-row stores (one store_b64 per
+    // key tile and column tile, issued after the copies; vector memory
+    // operations retire in issue order) may still be outstanding
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * TPW) : "memory");
     __syncthreads();
   }
