@@ -72,6 +72,25 @@ def test_forward_noalloc_two_calls_then_smaller(dsa):
     log(f"[no-alloc] oracle rows {rows.tolist()}: indices exact, attention max-abs {err:.2e}")
 
 
+def test_forward_noalloc_sampled_selection(dsa):
+    """A prefill-shaped problem with rows past 32K keys: the forward's
+    selection takes the sampled path (the indexer writes only candidate
+    keys), here inside the static scratch."""
+    wl = dsa_inputs.Workload("long_rows_mla", 42, 1, 64, 40000, 39936, 64, 128, 2048, 128, 512, 64)
+    prob = dsa.Problem.from_workload(wl)
+    plain = (4 * wl.q_len * wl.kv_len + 255) // 256 * 256 + dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
+    assert dsa.workspace_size(prob, dsa.DSA_OP_INDEX_TOPK) > plain, "the sampled path is taken"
+    inp, out, lse, idx = _both(dsa, wl)
+    rows = np.array([0, 31, 63])
+    rb, pos = dsa_inputs.row_batch_pos(wl, rows)
+    ref = oracle.forward(inp.k_idx, inp.q_idx[rows], inp.w[rows], inp.q[rows], inp.kv, rb, pos, wl.topk,
+                         wl.d_latent, wl.softmax_scale)
+    np.testing.assert_array_equal(idx.reshape(-1, wl.topk).cpu().numpy()[rows], ref["indices"])
+    err = np.abs(out.reshape(-1, wl.heads, wl.d_latent).cpu().numpy()[rows] - ref["out"]).max()
+    assert err <= 1e-2, err
+    log(f"[no-alloc] sampled selection: oracle rows {rows.tolist()} indices exact, attention max-abs {err:.2e}")
+
+
 def test_forward_noalloc_rejects_problems_beyond_the_scratch(dsa):
     wl = dsa_inputs.WORKLOADS["prefill32k"]
     prob = dsa.Problem.from_workload(wl)
