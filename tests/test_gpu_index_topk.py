@@ -15,6 +15,8 @@ Cases:
     their slots), only on them (too high: fewer than k candidates), every
     key equal (every row one big tie), one sequence of two tied, and a cache
     longer than the last query position;
+  * a prefill past 32K keys from position 0, whose first k rows select their
+    whole prefix while the last ones have 33,000 keys;
   * the chunked prefill (8192 queries at positions 122880..131071) and the
     chunked prefill over a 1M-token context, every row, plus dsa_forward on
     the former against the three stages.
@@ -136,6 +138,29 @@ def test_crafted_caches(dsa, case):
     assert_same_rows(label, got, ref)
     oracle_rows(label, inp, np.arange(wl.batch * wl.q_len), got)
     log(f"[{label}] all {wl.batch * wl.q_len} rows identical to the unfused path and the oracle")
+
+
+@pytest.mark.timeout(600)
+def test_prefill_past_32k_from_position_zero(dsa):
+    """Rows of every length in one sampled-path call: the first k rows select
+    their whole prefix (no threshold), the last ones have 33,000 keys."""
+    wl = dsa_inputs.Workload("prefill33k", 56, 1, 33000, 33000, 0, 64, 128, 2048, 8, 64, 16)
+    log(f"[prefill33k] B=1 Lq={wl.q_len} Lk={wl.kv_len} q_start=0")
+    inp = Inputs(wl, dsa_inputs.k_idx(wl), dsa_inputs.q_idx(wl), dsa_inputs.w(wl),
+                 np.zeros(0, np.uint16), np.zeros(0, np.uint16))
+    d = dict(q_idx=dev(inp.q_idx), k_idx=dev(inp.k_idx), w=dev(inp.w))
+    prob = dsa.Problem.from_workload(wl)
+    plain = (4 * wl.q_len * wl.kv_len + 255) // 256 * 256 + dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
+    assert dsa.workspace_size(prob, dsa.DSA_OP_INDEX_TOPK) > plain, "the sampled path is taken"
+    got = index_topk(dsa, prob, wl, d)
+    torch.cuda.empty_cache()
+    scores, ref = unfused(dsa, prob, wl, d)
+    del scores
+    torch.cuda.empty_cache()
+    assert_same_rows("prefill33k", got, ref)
+    rows = sorted({0, 1, 2046, 2047, 2048, 2049, 20000, 32767, 32768, 32999})
+    oracle_rows("prefill33k", inp, rows, got)
+    log(f"[prefill33k] every row identical to the unfused path; rows {rows} equal the oracle")
 
 
 @pytest.mark.timeout(900)
