@@ -240,19 +240,46 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
     int ln;
     asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
     uint32_t off[2][5] = {{0, 0, 0, 0, 0}, {0, 0, 0, 0, 0}};
+    // When the wave's blocks cover exactly the latent rows 8w .. 8w + 7 of
+    // the chunk (576-column rows: 9 blocks of 64 pieces = 8 rows of 72), block
+    // j1 spans at most rows t0 and t0 + 1 of them, split at lane `cut`, and
+    // the row's low 3 bits are its place among the eight; the eight indices
+    // come from two broadcast LDS reads instead of one look-up per block.
+    constexpr bool kEightRows = !MASKED && S::SWZ && BPW * 64 == 8 * S::PPR;
+    int rid[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (kEightRows) {
+      const v4i ia = *(const v4i*)(sidx + c * kChunk + 8 * wave);
+      const v4i ib = *(const v4i*)(sidx + c * kChunk + 8 * wave + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rid[e] = ia[e];
+        rid[4 + e] = ib[e];
+      }
+    }
 #pragma unroll
     for (int j1 = 0; j1 < BPW; ++j1) {
       const int run = j1 < R1 ? 0 : 1, j0 = j1 < R1 ? j1 : j1 - R1;
-      const uint32_t p = 64u * (uint32_t)(j_lo + j1) + (uint32_t)ln;
-      const uint32_t r = __umul24(p, div_mul(S::PPR)) >> kDivShift;
-      const uint32_t pp = p - r * (uint32_t)S::PPR;
-      const uint32_t lp = S::SWZ ? (pp ^ (r & 7u)) : pp;
+      uint32_t lp;  // logical piece of this lane's 16 bytes in its row
+      int idx;      // latent row index of that row
+      if constexpr (kEightRows) {
+        const int t0 = 64 * j1 / S::PPR;
+        const int cut = S::PPR * (t0 + 1) - 64 * j1;
+        const bool first = cut >= 64 || ln < cut;
+        const uint32_t t = first ? (uint32_t)t0 : (uint32_t)t0 + 1;
+        lp = (64u * (uint32_t)j1 + (uint32_t)ln - t * (uint32_t)S::PPR) ^ t;
+        idx = max(first ? rid[t0] : rid[t0 < 7 ? t0 + 1 : 7], 0);
+      } else {
+        const uint32_t p = 64u * (uint32_t)(j_lo + j1) + (uint32_t)ln;
+        const uint32_t r = __umul24(p, div_mul(S::PPR)) >> kDivShift;
+        const uint32_t pp = p - r * (uint32_t)S::PPR;
+        lp = S::SWZ ? (pp ^ (r & 7u)) : pp;
+        idx = MASKED ? min(kChunk * c + (int)r, n_keys - 1) : max(sidx[c * kChunk + r], 0);
+      }
       // Pad pieces (score width rounded up to 32) re-read real ones; they
       // meet zero q.  The swizzle keeps a piece inside its aligned group of
       // 8, so without padding every piece is a real one.
       uint32_t src_col = lp;
       if constexpr (S::PPR != S::RPR) src_col = lp < (uint32_t)S::RPR ? lp : lp - S::RPR;
-      const int idx = MASKED ? min(kChunk * c + (int)r, n_keys - 1) : max(sidx[c * kChunk + r], 0);
       // row indices are < 2^24 and the cache is < 4 GiB - 8 KiB (checked by the host)
       off[run][j0] = __umul24((uint32_t)idx, DQK * 2) + 16 * src_col + 4096 - 1024 * (j0 - 2);
     }
