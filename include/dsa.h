@@ -244,7 +244,7 @@ int dsa_sparse_mla_attn_ws(const dsa_problem* p, const uint16_t* q, const uint16
  *   workspace: at least dsa_workspace_size(p, DSA_OP_SPARSE_MLA_ATTN_BWD)
  *              bytes, 256-byte aligned; contents on return are unspecified.
  *              With R = B*Lq and kp = k rounded up to 32, it holds P and dZ
- *              (3 * R*kp*128 bf16), one partial dkv row per (row, entry)
+ *              (2 * R*kp*128 bf16), one partial dkv row per (row, entry)
  *              (R*kp*D_qk bf16) and the per-token lists of those entries
  *              (R*k + 3*B*Lk int32, plus one int32 per 4096 tokens), each
  *              part rounded up to 256 bytes.

@@ -13,15 +13,14 @@
 //   dkv[s_i] += scale * dz_i q  (+ p_i dout on the value columns).
 //
 // dq contracts over the keys and dkv over the heads, hence separate kernels:
-//  1. scores (one wave per 16 heads, 64 heads per block): the
+//  1. scores and dq (one wave per 16 heads, 64 heads per block): the
 //     selected latent rows are gathered into LDS in chunks of 32; S^T = K.Q^T
 //     and dP^T = V.dO^T run on bf16 MFMA sharing each K fragment read; P comes
-//     straight from the forward's lse, dZ = P (dP - D).  P and dZ go to the
-//     workspace in bf16, dZ once in the MFMA operand order of kernel 2 and
-//     both once key-major (dZ times scale) for kernel 3.
-//  2. dq (one block per row): dQ^T = K^T.dZ^T per chunk with the transposing
-//     K reads of the forward's value product; wave w owns d-tiles w, w+NW, ...
-//  3. dkv: per row, the partial product scale * dZ.Q + P.dO of every slot
+//     straight from the forward's lse, dZ = P (dP - D); then dQ^T += K^T.dZ^T
+//     from the same chunk with the transposing reads of the forward's value
+//     product, into accumulators held for the whole row.  P and dZ go to the
+//     workspace in bf16, key-major (dZ times scale), for kernel 2.
+//  2. dkv: per row, the partial product scale * dZ.Q + P.dO of every slot
 //     over the 128 heads on bf16 MFMA (one block per row, Q and dO held in
 //     registers), stored in bf16; per key, the sum over the (row, slot) pairs
 //     that list it (inverted lists built by count / scan / fill kernels), added
@@ -38,10 +37,10 @@ namespace {
 constexpr int kBChunk = 32;   // keys per chunk
 constexpr int kBTiles = 8;    // 128 heads / 16 (absent heads are zero)
 constexpr int kBHeads = 128;  // padded head count of the key-major buffers
-// per head tile and chunk, the scores kernel stores one 16-byte dZ fragment
-// and one 2-byte P and dZ value for each of a lane's 8 keys
+// per head tile and chunk, the scores kernel stores one 2-byte P and dZ value
+// for each of a lane's 8 keys
 constexpr int kScoreStoreKeys = 8;
-constexpr int kScoreStores = 1 + 2 * kScoreStoreKeys;
+constexpr int kScoreStores = 2 * kScoreStoreKeys;
 
 template <int DQK, int DV, int NW>
 struct BwdShape {
@@ -49,8 +48,7 @@ struct BwdShape {
   static constexpr int KST = DQKP / 32;              // k-steps of the score product
   static constexpr int KSTV = DV / 32;               // k-steps of the dout . v product
   static constexpr int HTQ = kBTiles / NW;           // 16-head tiles per wave
-  static constexpr int NDT = DQKP / 16;              // 16-column d-tiles
-  static constexpr int DTQ = (NDT + NW - 1) / NW;    // d-tiles per wave in the dq kernel
+  static constexpr int NDT = DQKP / 16;              // 16-column d-tiles of dq
   static constexpr int RS = DQKP * 2;                // LDS bytes per latent row
   static constexpr int PPR = RS / 16;                // 16-byte pieces per LDS row
   static constexpr int RPR = DQK * 2 / 16;           // pieces present in the cache row
@@ -166,12 +164,17 @@ __device__ __forceinline__ void stage_indices(const AttnBwdArgs& a, int row, int
   __syncthreads();
 }
 
-// ---- 1. scores: P and dZ of every (row, entry, head) -> workspace
+// ---- 1. scores and dq: P and dZ of every (row, entry, head) -> workspace,
+//         dq = scale * sum_i dZ_i kv_i -> dq
 // Q^T and dO^T of its heads stay in the wave's registers for the whole row
-// (72 + 64 per 16 heads at the 576/512 shape, more than two waves per SIMD
-// leave room for), so the kernel runs one wave per SIMD; the 8 head tiles
+// (72 + 64 per 16 heads at the 576/512 shape) and so do the fp32 dq
+// accumulators (144, matrix accumulator registers), more than two waves per
+// SIMD leave room for, so the kernel runs one wave per SIMD; the 8 head tiles
 // are split over SPLIT blocks of NW waves with HTQ tiles each.  The chunks are
-// copied straight into LDS, so no register holds the next chunk.
+// copied straight into LDS, so no register holds the next chunk.  The dq
+// products of a chunk read its K^T tiles four ahead: with one wave per SIMD
+// nothing else hides the read latency (without the prefetch the fused kernel
+// gained 3 % over a separate dq kernel, with it 12 %).
 template <int DQK, int DV, int NW, int SPLIT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_bwd_scores_kernel(AttnBwdArgs a) {
@@ -244,6 +247,20 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
   int k_off[2];
 #pragma unroll
   for (int par = 0; par < 2; ++par) k_off[par] = li * S::RS + bwd_piece<S>(li, 4 * par + g);
+  // dQ^T = K^T . dZ^T from the chunk in LDS: the A operand of d-tile t through
+  // the transposing reads of rows 4g + li/4 and 16 + 4g + li/4 (k-slots
+  // 8g..8g+7, the key order of the dZ fragment); four per-lane bases (t & 3)
+  // and a 128-byte step per four tiles reach every tile.
+  const int r_v0 = 4 * g + (li >> 2);
+  int v_off[4];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4)
+    v_off[q4] = r_v0 * S::RS + 8 * (li & 1) + bwd_piece<S>(r_v0, 2 * q4 + ((li & 3) >> 1));
+  v4f dacc[S::HTQ][S::NDT];
+#pragma unroll
+  for (int ht = 0; ht < S::HTQ; ++ht)
+#pragma unroll
+    for (int t = 0; t < S::NDT; ++t) dacc[ht][t] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
 
   const uint8_t* seq = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK);
   dma_chunk<S, NW>(kvb, seq, sidx, wave_b);
@@ -303,10 +320,27 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
           pv[4 * kt + r] = p;
           zv[4 * kt + r] = p * (pacc[ht][kt][r] - Dh[ht]);
         }
-      // dZ in the B-operand order of the dq kernel (k-slots 8g..8g+7)
+      // dZ in bf16 as the B operand of dQ^T += K^T . dZ^T (k-slots 8g..8g+7)
       const v4i zf = {(int)pack_bf16x2(zv[0], zv[1]), (int)pack_bf16x2(zv[2], zv[3]),
                       (int)pack_bf16x2(zv[4], zv[5]), (int)pack_bf16x2(zv[6], zv[7])};
-      store_b128(a.ws_dzf + ((((size_t)row * nch + c) * kBTiles + tile) * 64 + lane) * 8, zf);
+      const v8bf zb = __builtin_bit_cast(v8bf, zf);
+      auto load_kt = [&](int t) {
+        const int voff = v_off[t & 3] + 128 * (t >> 2);
+        const v4s lo = lds_read_tr16(kb + voff);
+        const v4s hi = lds_read_tr16(kb + voff + 16 * S::RS);
+        return __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      };
+      constexpr int kTPre = 4;  // K^T tiles read ahead
+      v8bf ktp[kTPre + 1];
+#pragma unroll
+      for (int t = 0; t < kTPre && t < S::NDT; ++t) ktp[t] = load_kt(t);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < S::NDT; ++t) {
+        if (t + kTPre < S::NDT) ktp[(t + kTPre) % (kTPre + 1)] = load_kt(t + kTPre);
+        dacc[ht][t] = mfma_bf16_16x16x32(ktp[t % (kTPre + 1)], zb, dacc[ht][t]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // P and scale * dZ key-major [row][slot][128 heads] for the dkv products
       const int ln = opaque_tid() & 63;
       const size_t kmbase = ((size_t)row * kpad + (size_t)c * kBChunk + 4 * (ln >> 4)) * kBHeads +
@@ -326,109 +360,21 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kScoreStores * S::HTQ) : "memory");
     __syncthreads();
   }
-}
 
-// ---- 2. dq = scale * sum_i dZ_i kv_i
-template <int DQK, int DV, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(AttnBwdArgs a) {
-  using S = BwdShape<DQK, DV, NW>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint8_t* kvb = smem;                                        // [2][CHUNK_BYTES]
-  uint8_t* zbuf = smem + 2 * S::CHUNK_BYTES;                  // [2][8 tiles][64 lanes][16 B]
-  int32_t* sidx = (int32_t*)(zbuf + 2 * kBTiles * 1024);      // [nch * 32]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = lane >> 4, li = lane & 15;
-  const int row = blockIdx.x;
-  const int b = row / a.Lq;
-  const int nch = (a.k + kBChunk - 1) / kBChunk;
-  stage_indices(a, row, nch, sidx);
-
-  // A operand (K^T of d-tile t) through the transposing reads of the
-  // forward's value product: rows 4g + li/4 and 16 + 4g + li/4 of the chunk
-  // give the k-slots 8g..8g+7 in the key order the dZ fragments use.
-  const int r_v0 = 4 * g + (li >> 2);
-  const int v_base = r_v0 * S::RS + 8 * (li & 1);
-  const int v_sel = (li & 3) >> 1;
-
-  const uint8_t* seq = (const uint8_t*)(a.kv + (size_t)b * a.Lk * DQK);
-  const v4i* zsrc = (const v4i*)(a.ws_dzf + (size_t)row * nch * kBTiles * 64 * 8);
-  constexpr int ZPER = (kBTiles * 64 + S::NT - 1) / S::NT;  // dZ pieces per thread
-  ChunkRegs<S> cr;
-  v4i zr[ZPER];
-  auto load_z = [&](int c) {
+  // dq of this wave's heads: lane holds d = 16t + 4g + r of head 16*tile + li
 #pragma unroll
-    for (int j = 0; j < ZPER; ++j) {
-      const int p = threadIdx.x + j * S::NT;
-      if (p < kBTiles * 64) zr[j] = zsrc[(size_t)c * kBTiles * 64 + p];
-    }
-  };
-  auto store_z = [&](int buf) {
+  for (int ht = 0; ht < S::HTQ; ++ht) {
+    const int head = 16 * (S::HTQ * wave + ht) + li;
+    if (head >= a.H) continue;
 #pragma unroll
-    for (int j = 0; j < ZPER; ++j) {
-      const int p = threadIdx.x + j * S::NT;
-      if (p < kBTiles * 64) *(v4i*)(zbuf + buf * kBTiles * 1024 + 16 * p) = zr[j];
-    }
-  };
-  cr.load(seq, sidx);
-  load_z(0);
-  cr.store(kvb);
-  store_z(0);
-  __syncthreads();
-
-  v4f acc[S::DTQ][kBTiles];
-#pragma unroll
-  for (int j = 0; j < S::DTQ; ++j)
-#pragma unroll
-    for (int ht = 0; ht < kBTiles; ++ht) acc[j][ht] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    const uint8_t* kb = kvb + buf * S::CHUNK_BYTES;
-    if (c + 1 < nch) {
-      cr.load(seq, sidx + (c + 1) * kBChunk);
-      load_z(c + 1);
-    }
-    v8bf kt_[S::DTQ];
-#pragma unroll
-    for (int j = 0; j < S::DTQ; ++j) {
-      const int t = wave + NW * j;
-      const int tt = t < S::NDT ? t : 0;  // tiles past the width are not stored
-      const int voff = v_base + bwd_piece<S>(r_v0, 2 * tt + v_sel);
-      const v4s lo = lds_read_tr16(kb + voff);
-      const v4s hi = lds_read_tr16(kb + voff + 16 * S::RS);
-      kt_[j] = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-    }
-#pragma unroll
-    for (int ht = 0; ht < kBTiles; ++ht) {
-      const v8bf zf = __builtin_bit_cast(v8bf, *(const v4i*)(zbuf + buf * kBTiles * 1024 + ht * 1024 + 16 * lane));
-#pragma unroll
-      for (int j = 0; j < S::DTQ; ++j) acc[j][ht] = mfma_bf16_16x16x32(kt_[j], zf, acc[j][ht]);
-    }
-    __syncthreads();
-    if (c + 1 < nch) {
-      cr.store(kvb + ((c + 1) & 1) * S::CHUNK_BYTES);
-      store_z((c + 1) & 1);
-      __syncthreads();
-    }
-  }
-
-  // lane: d = 16t + 4g + r, head 16ht + li
-#pragma unroll
-  for (int j = 0; j < S::DTQ; ++j) {
-    const int t = wave + NW * j;
-    const int d0 = 16 * t + 4 * g;
-    if (t >= S::NDT || d0 >= DQK) continue;
-#pragma unroll
-    for (int ht = 0; ht < kBTiles; ++ht) {
-      const int head = 16 * ht + li;
-      if (head < a.H) *(v4f*)(a.dq + ((size_t)row * a.H + head) * DQK + d0) = acc[j][ht] * a.scale;
+    for (int t = 0; t < S::NDT; ++t) {
+      const int d0 = 16 * t + 4 * g;
+      if (d0 < DQK) *(v4f*)(a.dq + ((size_t)row * a.H + head) * DQK + d0) = dacc[ht][t] * a.scale;
     }
   }
 }
 
-// ---- 3. dkv[s] += sum over the (row, slot) pairs listing s of
+// ---- 2. dkv[s] += sum over the (row, slot) pairs listing s of
 //         scale * dZ[slot,:] . Q + P[slot,:] . dO        (contracted over heads)
 // Fp32 atomics into dkv run at about one element per L2 channel and clock,
 // far below the rate the partial products are made at, so the reduction goes
@@ -745,7 +691,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_reduce_kernel(AttnBwdArgs a)
 
 // Workspace layout (byte offsets, each part 256-byte aligned).
 struct BwdLayout {
-  size_t dzf, pk, dzk, part, list, cnt, off, cur, bsum, total;
+  size_t pk, dzk, part, list, cnt, off, cur, bsum, total;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -756,8 +702,7 @@ BwdLayout bwd_layout(int B, int Lq, int Lk, int k, int dqk) {
   const size_t keys = (size_t)B * Lk;
   const size_t hm = align256(rows * kpad * kBHeads * sizeof(uint16_t));
   BwdLayout l{};
-  l.dzf = 0;
-  l.pk = l.dzf + hm;
+  l.pk = 0;
   l.dzk = l.pk + hm;
   l.part = l.dzk + hm;
   l.list = l.part + align256(rows * kpad * dqk * sizeof(uint16_t));
@@ -769,23 +714,18 @@ BwdLayout bwd_layout(int B, int Lq, int Lk, int k, int dqk) {
   return l;
 }
 
-// Scores kernel: SPLIT blocks of NW1 waves per row; dq kernel: NW2 waves;
+// Scores (and dq) kernel: SPLIT blocks of NW1 waves per row;
 // partial-product kernel: NW3 waves with TPW column tiles each.
-template <int DQK, int DV, int NW1, int SPLIT, int NW2, int NW3, int TPW>
+template <int DQK, int DV, int NW1, int SPLIT, int NW3, int TPW>
 hipError_t launch_bwd_shape(const AttnBwdArgs& a, hipStream_t stream) {
   using S1 = BwdShape<DQK, DV, NW1 * SPLIT>;
-  using S2 = BwdShape<DQK, DV, NW2>;
   const int nch = (a.k + kBChunk - 1) / kBChunk;
   const size_t sidx_bytes = (size_t)nch * kBChunk * sizeof(int32_t);
   const size_t smem1 = 2 * (size_t)S1::CHUNK_BYTES + sidx_bytes;
-  const size_t smem2 = 2 * (size_t)S2::CHUNK_BYTES + 2 * kBTiles * 1024 + sidx_bytes;
   static const hipError_t attr1 = hipFuncSetAttribute(
       (const void*)attn_bwd_scores_kernel<DQK, DV, NW1, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
       160 * 1024);
-  static const hipError_t attr2 = hipFuncSetAttribute(
-      (const void*)attn_bwd_dq_kernel<DQK, DV, NW2>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (attr1 != hipSuccess) return attr1;
-  if (attr2 != hipSuccess) return attr2;
   const unsigned rows = (unsigned)((long long)a.B * a.Lq);
   const long long entries = (long long)rows * a.k;
   const long long keys = (long long)a.B * a.Lk;
@@ -811,9 +751,6 @@ hipError_t launch_bwd_shape(const AttnBwdArgs& a, hipStream_t stream) {
   if ((e = launch_kernel((const void*)attn_bwd_scores_kernel<DQK, DV, NW1, SPLIT>, dim3(rows * SPLIT), dim3(64 * NW1),
                          smem1, stream, a)) != hipSuccess)
     return e;
-  if ((e = launch_kernel((const void*)attn_bwd_dq_kernel<DQK, DV, NW2>, dim3(rows), dim3(64 * NW2), smem2, stream,
-                         a)) != hipSuccess)
-    return e;
   if ((e = launch_kernel((const void*)attn_bwd_dkv_part_kernel<DQK, DV, NW3, TPW>, dim3(rows), dim3(64 * NW3), 0,
                          stream, a)) != hipSuccess)
     return e;
@@ -831,7 +768,6 @@ hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& args, void* workspace, 
   AttnBwdArgs a = args;
   const BwdLayout l = bwd_layout(a.B, a.Lq, a.Lk, a.k, a.Dv + a.Dr);
   uint8_t* w = (uint8_t*)workspace;
-  a.ws_dzf = (uint16_t*)(w + l.dzf);
   a.ws_pk = (uint16_t*)(w + l.pk);
   a.ws_dzk = (uint16_t*)(w + l.dzk);
   a.ws_part = (uint16_t*)(w + l.part);
@@ -840,8 +776,8 @@ hipError_t launch_sparse_mla_attn_bwd(const AttnBwdArgs& args, void* workspace, 
   a.ws_off = (int32_t*)(w + l.off);
   a.ws_cur = (int32_t*)(w + l.cur);
   a.ws_bsum = (int32_t*)(w + l.bsum);
-  if (a.Dv == 512 && a.Dr == 64) return launch_bwd_shape<576, 512, 4, 2, 8, 12, 3>(a, stream);
-  if (a.Dv == 64 && a.Dr == 16) return launch_bwd_shape<80, 64, 4, 1, 4, 5, 1>(a, stream);
+  if (a.Dv == 512 && a.Dr == 64) return launch_bwd_shape<576, 512, 4, 2, 12, 3>(a, stream);
+  if (a.Dv == 64 && a.Dr == 16) return launch_bwd_shape<80, 64, 4, 1, 5, 1>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -90,7 +90,6 @@ struct AttnBwdArgs {
   // dZ in operand order, P and scale * dZ key-major ([B*Lq, kpad, 128] bf16),
   // partial dkv rows per (row, slot) ([B*Lq, kpad, Dqk] bf16), the (row, slot)
   // lists of every key with their counts and offsets, scan block sums
-  uint16_t* ws_dzf;
   uint16_t* ws_pk;
   uint16_t* ws_dzk;
   uint16_t* ws_part;

@@ -165,7 +165,7 @@ def _bwd_ws(B, Lq, Lk, k, dqk):
     # the sizes dsa.h documents for the backward's workspace
     r, kp = B * Lq, -(-k // 32) * 32
     up = lambda x: -(-x // 256) * 256  # noqa: E731
-    return (3 * up(r * kp * 128 * 2) + up(r * kp * dqk * 2) + up(r * k * 4) + 3 * up(B * Lk * 4)
+    return (2 * up(r * kp * 128 * 2) + up(r * kp * dqk * 2) + up(r * k * 4) + 3 * up(B * Lk * 4)
             + up(-(-(B * Lk) // 4096) * 4))
 
 
@@ -174,8 +174,8 @@ def test_backward_checks():
     assert dsa.workspace_size(MLA, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == _bwd_ws(1, 4096, 4096, 2048, 576)
     odd = Problem(**{**GOOD.__dict__, "topk": 65})
     assert dsa.workspace_size(odd, dsa.DSA_OP_SPARSE_MLA_ATTN_BWD) == _bwd_ws(1, 256, 256, 65, 80)
-    # padded entries: 3 * rows * 96 * 128 bf16 of P / dZ for k = 65
-    assert _bwd_ws(1, 256, 256, 65, 80) > 3 * 256 * 96 * 128 * 2
+    # padded entries: 2 * rows * 96 * 128 bf16 of P / dZ for k = 65
+    assert _bwd_ws(1, 256, 256, 65, 80) > 2 * 256 * 96 * 128 * 2
     # the lists index (row, entry) pairs in 32 bits
     huge = Problem(8, 131072, 131072, 0, 64, 128, 2048, 128, 512, 64)
     with pytest.raises(DsaError):
