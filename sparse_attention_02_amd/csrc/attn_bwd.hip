@@ -37,10 +37,12 @@ namespace {
 constexpr int kBChunk = 32;   // keys per chunk
 constexpr int kBTiles = 8;    // 128 heads / 16 (absent heads are zero)
 constexpr int kBHeads = 128;  // padded head count of the key-major buffers
-// per head tile and chunk, the scores kernel stores one 2-byte P and dZ value
-// for each of a lane's 8 keys
+// per head tile and chunk, the scores kernel holds P and dZ of 8 keys per lane
+// and stores the tile's P and dZ (32 keys x 16 heads each) with one 16-byte
+// store apiece, after a transpose through LDS
 constexpr int kScoreStoreKeys = 8;
-constexpr int kScoreStores = 2 * kScoreStoreKeys;
+constexpr int kScoreStores = 2;
+constexpr int kStageBytes = 2 * kBChunk * 16 * 2;  // per wave: [P, dZ][32 keys][16 heads] bf16
 
 template <int DQK, int DV, int NW>
 struct BwdShape {
@@ -90,9 +92,6 @@ __device__ __forceinline__ void store_b128(void* p, v4i v) {
 }
 __device__ __forceinline__ void store_b64(void* p, v2i v) {
   asm volatile("global_store_dwordx2 %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ void store_b16(void* p, uint32_t v) {
-  asm volatile("global_store_short %0, %1, off\n\ts_nop 1" :: "v"(p), "v"(v) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -182,6 +181,9 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   uint8_t* kvb = smem;                                   // [2][CHUNK_BYTES]
   int32_t* sidx = (int32_t*)(smem + 2 * S::CHUNK_BYTES);  // [nch * 32]
+  // per wave: P and dZ of a head tile, key-major, for the 16-byte stores
+  uint16_t* stg = (uint16_t*)(smem + 2 * S::CHUNK_BYTES + (size_t)((a.k + kBChunk - 1) / kBChunk) * kBChunk * 4 +
+                              kStageBytes * (threadIdx.x >> 6));
 
   const int lane = threadIdx.x & 63;
   const int wave_b = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave in the block
@@ -341,16 +343,22 @@ void attn_bwd_scores_kernel(AttnBwdArgs a) {
         dacc[ht][t] = mfma_bf16_16x16x32(ktp[t % (kTPre + 1)], zb, dacc[ht][t]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // P and scale * dZ key-major [row][slot][128 heads] for the dkv products
-      const int ln = opaque_tid() & 63;
-      const size_t kmbase = ((size_t)row * kpad + (size_t)c * kBChunk + 4 * (ln >> 4)) * kBHeads +
-                            16 * tile + (ln & 15);
+      // P and scale * dZ key-major [row][slot][128 heads] for the dkv
+      // products: the tile goes through the wave's LDS stage ([32 keys][16
+      // heads] each), then lane 2k + u stores heads 8u .. 8u + 7 of key k
+      // (LDS operations of one wave complete in order, so no barrier)
 #pragma unroll
       for (int e = 0; e < kScoreStoreKeys; ++e) {
-        const size_t o = kmbase + (size_t)(16 * (e >> 2) + (e & 3)) * kBHeads;
-        store_b16(a.ws_pk + o, pack_bf16x2(pv[e], 0.0f) & 0xFFFFu);
-        store_b16(a.ws_dzk + o, pack_bf16x2(zv[e] * a.scale, 0.0f) & 0xFFFFu);
+        const int key = 16 * (e >> 2) + 4 * g + (e & 3);
+        stg[key * 16 + li] = (uint16_t)(pack_bf16x2(pv[e], 0.0f) & 0xFFFFu);
+        stg[kBChunk * 16 + key * 16 + li] = (uint16_t)(pack_bf16x2(zv[e] * a.scale, 0.0f) & 0xFFFFu);
       }
+      const int ln = opaque_tid() & 63;
+      const v4i pst = *(const v4i*)(stg + 8 * ln);
+      const v4i zst = *(const v4i*)(stg + kBChunk * 16 + 8 * ln);
+      const size_t o = ((size_t)row * kpad + (size_t)c * kBChunk + (ln >> 1)) * kBHeads + 16 * tile + 8 * (ln & 1);
+      store_b128(a.ws_pk + o, pst);
+      store_b128(a.ws_dzk + o, zst);
     }
     // the next chunk's copies are complete and every wave is done with this
     // one.  Vector memory operations retire in issue order, so waiting until
@@ -721,7 +729,7 @@ hipError_t launch_bwd_shape(const AttnBwdArgs& a, hipStream_t stream) {
   using S1 = BwdShape<DQK, DV, NW1 * SPLIT>;
   const int nch = (a.k + kBChunk - 1) / kBChunk;
   const size_t sidx_bytes = (size_t)nch * kBChunk * sizeof(int32_t);
-  const size_t smem1 = 2 * (size_t)S1::CHUNK_BYTES + sidx_bytes;
+  const size_t smem1 = 2 * (size_t)S1::CHUNK_BYTES + sidx_bytes + (size_t)NW1 * kStageBytes;
   static const hipError_t attr1 = hipFuncSetAttribute(
       (const void*)attn_bwd_scores_kernel<DQK, DV, NW1, SPLIT>, hipFuncAttributeMaxDynamicSharedMemorySize,
       160 * 1024);
