@@ -12,14 +12,17 @@
 // fp32 accumulation (exact whenever the fp32 sum is, as on the input grids);
 // c is rounded to bf16 for the two products.  Two kernels:
 //  1. query-stationary (block = 4 query rows x 64 heads, 8 waves of one row
-//     and 32 heads): key tiles of 32 are staged in LDS as bf16 both
-//     key-major (for u^T = K.Q^T) and d-major (for dq^T = K^T.c^T); a lane's
-//     8 keys of a c^T fragment are the 8 keys the u^T tile left in it, so the
-//     d-major reads take the same key order.
+//     and 32 heads): key tiles of 32 are staged in LDS as bf16, key-major;
+//     u^T = K.Q^T reads them directly and dq^T = K^T.c^T through the
+//     transposing LDS reads; a lane's 8 keys of a c^T fragment are the 8 keys
+//     the u^T tile left in it, so the transposing reads take the same order.
 //  2. key-stationary (block = 256 keys in registers, 32 per wave, x a range of
-//     query rows): each row's q_I is staged as bf16 head-major (u = Q.K^T) and
-//     d-major (dk^T = Q^T.c), and the block's partial dk_I goes to memory with
-//     one fp32 atomic add per element at the end.
+//     query rows): each row's q_I is staged as bf16 head-major, read directly
+//     for u = Q.K^T and through the transposing reads for dk^T = Q^T.c, and
+//     the block's partial dk_I goes to memory with one fp32 atomic add per
+//     element at the end.
+// (A second, d-major copy of each staged tile written with 2-byte stores
+// took the transposed operands before: 69 ms at the 32K prefill against 54.)
 #include <algorithm>
 
 #include "dsa_common.h"
@@ -48,8 +51,6 @@ __device__ __forceinline__ v4i e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 constexpr int kQRows = 4;     // query rows per block of kernel 1
 constexpr int kKeysPerBlock = 256;
-constexpr int kTRow = 36;     // d-major key tile row: 32 keys + 4 pad (bf16)
-constexpr int kHRow = 68;     // d-major head row: 64 heads + 4 pad (bf16)
 
 // piece p (8 dims) of row k of a key-major / head-major bf16 tile with NP
 // pieces per row: XOR-swizzled when NP is a power of two
@@ -63,7 +64,6 @@ template <int DI>
 __global__ __launch_bounds__(512) void index_bwd_q_kernel(IndexBwdArgs a) {
   constexpr int KST = DI / 32, NDT = DI / 16, NP = DI / 8;
   __shared__ __attribute__((aligned(16))) uint16_t kb[2][32 * DI];      // [key][d] (swizzled pieces)
-  __shared__ __attribute__((aligned(16))) uint16_t ktr[2][DI * kTRow];  // [d][key]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, li = lane & 15;
@@ -105,12 +105,13 @@ __global__ __launch_bounds__(512) void index_bwd_q_kernel(IndexBwdArgs a) {
     if (!stager) return;
     const v4i v = e4m3x8_to_bf16(raw.x, raw.y);
     *(v4i*)&kb[st][sk * DI + 8 * swz<NP>(sp, sk)] = v;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ktr[st][(8 * sp + 2 * i) * kTRow + sk] = (uint16_t)(v[i] & 0xFFFF);
-      ktr[st][(8 * sp + 2 * i + 1) * kTRow + sk] = (uint16_t)((uint32_t)v[i] >> 16);
-    }
   };
+  // K^T fragments through the transposing reads: group g's lanes address key
+  // rows 4g + li/4 (and 16 + 4g + li/4), 4 dims each at d = 16dt + 4(li&3),
+  // so lane li receives d = 16dt + li for the keys 4g..4g+3 (16 + ..): the
+  // k-slots 8g..8g+7 in the key order of the c^T fragment
+  const int tr_key = 4 * g + (li >> 2);
+  const int tr_sel = (li & 3) >> 1, tr_half = 8 * (li & 1);
 
   v4f acc[2][NDT];
 #pragma unroll
@@ -168,9 +169,11 @@ __global__ __launch_bounds__(512) void index_bwd_q_kernel(IndexBwdArgs a) {
       // dq^T += K^T . c^T: A lane (d = 16dt + li) holds the same 8 keys
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const uint16_t* kr = &ktr[st][(16 * dt + li) * kTRow];
-        const uint2 lo = *(const uint2*)(kr + 4 * g), hi = *(const uint2*)(kr + 16 + 4 * g);
-        const v8bf ka = __builtin_bit_cast(v8bf, (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y});
+        const int pc = swz<NP>(2 * dt + tr_sel, tr_key);  // same for rows tr_key and tr_key + 16
+        const uint8_t* kr = (const uint8_t*)&kb[st][tr_key * DI] + 16 * pc + tr_half;
+        const v4s lo = lds_read_tr16(kr);
+        const v4s hi = lds_read_tr16(kr + 16 * DI * 2);
+        const v8bf ka = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
         for (int ht = 0; ht < 2; ++ht) acc[ht][dt] = mfma_bf16_16x16x32(ka, cb[ht], acc[ht][dt]);
       }
@@ -200,7 +203,6 @@ template <int DI>
 __global__ __launch_bounds__(512) void index_bwd_k_kernel(IndexBwdArgs a, int rows_per_block) {
   constexpr int KST = DI / 32, NDT = DI / 16, NP = DI / 8, NP16 = DI / 16;
   __shared__ __attribute__((aligned(16))) uint16_t qa[2][64 * DI];     // [head][d] (swizzled pieces)
-  __shared__ __attribute__((aligned(16))) uint16_t qt[2][DI * kHRow];  // [d][head]
   __shared__ float ws[2][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -249,13 +251,13 @@ __global__ __launch_bounds__(512) void index_bwd_k_kernel(IndexBwdArgs a, int ro
       const v4i v = e4m3x8_to_bf16(hf ? raw.z : raw.x, hf ? raw.w : raw.y);
       const int p = 2 * sq + hf;
       *(v4i*)&qa[st][sh * DI + 8 * swz<NP>(p, sh)] = v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        qt[st][(8 * p + 2 * i) * kHRow + sh] = (uint16_t)(v[i] & 0xFFFF);
-        qt[st][(8 * p + 2 * i + 1) * kHRow + sh] = (uint16_t)((uint32_t)v[i] >> 16);
-      }
     }
   };
+  // Q^T fragments through the transposing reads: group g's lanes address head
+  // rows 32hs + 4g + li/4 (and + 16), 4 dims each at d = 16dt + 4(li&3), so
+  // lane li receives d = 16dt + li for the k-slots 8g..8g+7 of the c fragment
+  const int tr_head = 4 * g + (li >> 2);
+  const int tr_sel = (li & 3) >> 1, tr_half = 8 * (li & 1);
 
   v4f acc[2][NDT];
 #pragma unroll
@@ -311,11 +313,13 @@ __global__ __launch_bounds__(512) void index_bwd_k_kernel(IndexBwdArgs a, int ro
       // dk^T += Q^T . c: A lane (d = 16dt + li) holds the same 8 heads
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const uint16_t* qr = &qt[st][(16 * dt + li) * kHRow];
+        const int pc = swz<NP>(2 * dt + tr_sel, tr_head);  // same for every head row the lane reads
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          const uint2 lo = *(const uint2*)(qr + 32 * hs + 4 * g), hi = *(const uint2*)(qr + 32 * hs + 16 + 4 * g);
-          const v8bf qa8 = __builtin_bit_cast(v8bf, (v4i){(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y});
+          const uint8_t* qr = (const uint8_t*)&qa[st][(32 * hs + tr_head) * DI] + 16 * pc + tr_half;
+          const v4s lo = lds_read_tr16(qr);
+          const v4s hi = lds_read_tr16(qr + 16 * DI * 2);
+          const v8bf qa8 = __builtin_bit_cast(v8bf, (v8s_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) acc[kt][dt] = mfma_bf16_16x16x32(qa8, cb[hs][kt], acc[kt][dt]);
         }
