@@ -137,17 +137,21 @@ __global__ __launch_bounds__(64 * kWWaves) void warmup_target_kernel(WarmupArgs 
     for (int ht = 0; ht < kWHt; ++ht)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) acc[ht][kt] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+    // k-steps outermost: the four accumulators take turns, so a product
+    // never waits on the one just issued
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int kr = 16 * kt + li;
-      const uint8_t* rowp = &kbuf[st][kr * S::RS];
+    for (int ks = 0; ks < S::KST; ++ks) {
+      const int lp = 4 * ks + g;
+      v8bf kf[2];
 #pragma unroll
-      for (int ks = 0; ks < S::KST; ++ks) {
-        const int lp = 4 * ks + g;
-        const v8bf kf = __builtin_bit_cast(v8bf, *(const v4i*)(rowp + 16 * (S::SWZ ? (lp ^ (kr & 7)) : lp)));
-#pragma unroll
-        for (int ht = 0; ht < kWHt; ++ht) acc[ht][kt] = mfma_bf16_16x16x32(qf[ht][ks], kf, acc[ht][kt]);
+      for (int kt = 0; kt < 2; ++kt) {
+        const int kr = 16 * kt + li;
+        kf[kt] = __builtin_bit_cast(v8bf, *(const v4i*)(&kbuf[st][kr * S::RS] + 16 * (S::SWZ ? (lp ^ (kr & 7)) : lp)));
       }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ht = 0; ht < kWHt; ++ht) acc[ht][kt] = mfma_bf16_16x16x32(qf[ht][ks], kf[kt], acc[ht][kt]);
     }
   };
 
