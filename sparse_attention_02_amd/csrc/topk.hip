@@ -232,12 +232,6 @@ struct BlockSelect {
   uint32_t* scan_sh;
   uint32_t* ctrl;
 
-  __device__ __forceinline__ uint32_t sum(uint32_t v) {
-    uint32_t total;
-    block_inclusive_scan_n<NT>(v, scan_sh, total);
-    return total;
-  }
-
   // One digit pass: histogram of the digit (r >> shift) & dmask of the keys
   // key[j < cnt] with r >> cur == pref (r = key - kmin; every key when cur is
   // 32), then the digit holding the need-th largest of them.  Returns the
@@ -399,7 +393,6 @@ __device__ __forceinline__ void select_top(BlockSelect<NT> sel, uint32_t (&key)[
   constexpr int E2 = kCap / NT;   // candidates per thread in the exact selection
   const int base = EPT * (int)threadIdx.x;
   uint32_t t = 0;  // every key is >= 0
-  bool filtered = true;
   if (n > kCap) {
     uint32_t smp[S];
 #pragma unroll
@@ -409,21 +402,20 @@ __device__ __forceinline__ void select_top(BlockSelect<NT> sel, uint32_t (&key)[
     const float qm = (float)k * (float)m / (float)n;
     const uint32_t r = min(m, (uint32_t)(qm + 4.0f * sqrtf(qm) + 8.0f));
     t = sel.coarse_threshold(smp, scnt, r);
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < EPT; ++j) c += j < cnt && key[j] >= t;
-    c = sel.sum(c);
-    filtered = c >= k && c <= (uint32_t)kCap;
   }
-  if (filtered) {
-    // recomputed below rather than kept from the count: 64 live predicates
-    // would cost as many registers as the keys
-    asm volatile("" : "+v"(t));
-    uint32_t mine = 0;
+  // One scan of the per-thread counts of keys >= t gives both the total (is
+  // the cut usable: at least k and at most kCap candidates) and each
+  // thread's place in the compaction.
+  uint32_t mine = 0;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) mine += j < cnt && key[j] >= t;
-    uint32_t total;
-    uint32_t o = block_inclusive_scan_n<NT>(mine, sel.scan_sh, total) - mine;
+  for (int j = 0; j < EPT; ++j) mine += j < cnt && key[j] >= t;
+  uint32_t total;
+  uint32_t o = block_inclusive_scan_n<NT>(mine, sel.scan_sh, total) - mine;
+  const bool filtered = total >= k && total <= (uint32_t)kCap;  // block-uniform
+  if (filtered) {
+    // the predicates are recomputed rather than kept from the count: 64 live
+    // ones would cost as many registers as the keys
+    asm volatile("" : "+v"(t));
 #pragma unroll
     for (int j = 0; j < EPT; ++j)
       if (j < cnt && key[j] >= t) {
