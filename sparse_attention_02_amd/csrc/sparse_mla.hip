@@ -164,39 +164,18 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   // chunks [c_lo, c_hi) of the row belong to this block
   const int c_lo = part * nch / a.nsplit, c_hi = (part + 1) * nch / a.nsplit;
 
-  uint64_t chunk_mask = 0, full_mask = 0;  // sparse: chunks with some / with only valid entries
-  const int32_t* idx_row = a.indices + (size_t)row * a.k;
-  if constexpr (MASKED) {
-    // ---- selection bitmap of this block's chunks (entries outside its key
-    // range, past pos(t) included, are not set; a repeated entry counts once)
-    for (int i = c_lo + threadIdx.x; i < c_hi; i += blockDim.x) selm[i] = 0u;
-    __syncthreads();
-    const int s_lo = kChunk * c_lo, s_hi = min(kChunk * c_hi, n_keys);
-    for (int i = threadIdx.x; i < a.k; i += blockDim.x) {
-      const int v = idx_row[i];
-      if (v >= s_lo && v < s_hi) atomicOr(&selm[v / kChunk], 1u << (v % kChunk));
-    }
-    __syncthreads();
-  } else {
-    // ---- selected indices -> LDS (entries outside [0, Lk) become -1)
-    for (int i = c_lo * kChunk + threadIdx.x; i < c_hi * kChunk; i += blockDim.x) {
-      const int v = i < a.k ? idx_row[i] : -1;
-      sidx[i] = (v >= 0 && v < a.Lk) ? v : -1;
-    }
-    __syncthreads();
-    const bool mine = lane >= c_lo && lane < c_hi;
-    bool any = false, all = mine;
-    if (mine)
-      for (int j = 0; j < kChunk; ++j) {
-        const bool v = sidx[lane * kChunk + j] >= 0;
-        any |= v;
-        all &= v;
-      }
-    chunk_mask = __ballot(any);
-    full_mask = __ballot(all);
+  // sparse mode: the row's selected indices, loaded ahead of Q (k <= 64 chunks)
+  const int32_t* idx_row0 = a.indices + (size_t)row * a.k;
+  constexpr int kIdxPer = (64 * kChunk + 64 * NW - 1) / (64 * NW);
+  int iv[kIdxPer];
+#pragma unroll
+  for (int j = 0; j < kIdxPer; ++j) {
+    const int i = c_lo * kChunk + (int)threadIdx.x + j * (int)blockDim.x;
+    iv[j] = (!MASKED && i < c_hi * kChunk) ? (i < a.k ? idx_row0[i] : -1) : 0;
   }
 
-  // ---- Q^T fragments of this wave's heads (B operand of the score products)
+  // ---- Q^T fragments of this wave's heads (B operand of the score products),
+  // loaded first so that their latency overlaps the index staging below
   v8bf qf[S::HTQ][S::KST];
 #pragma unroll
   for (int ht = 0; ht < S::HTQ; ++ht) {
@@ -211,6 +190,40 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
       if (!ok) v = (v4i){0, 0, 0, 0};
       qf[ht][ks] = __builtin_bit_cast(v8bf, v);
     }
+  }
+
+  uint64_t chunk_mask = 0, full_mask = 0;  // sparse: chunks with some / with only valid entries
+  const int32_t* idx_row = a.indices + (size_t)row * a.k;
+  if constexpr (MASKED) {
+    // ---- selection bitmap of this block's chunks (entries outside its key
+    // range, past pos(t) included, are not set; a repeated entry counts once)
+    for (int i = c_lo + threadIdx.x; i < c_hi; i += blockDim.x) selm[i] = 0u;
+    __syncthreads();
+    const int s_lo = kChunk * c_lo, s_hi = min(kChunk * c_hi, n_keys);
+    for (int i = threadIdx.x; i < a.k; i += blockDim.x) {
+      const int v = idx_row[i];
+      if (v >= s_lo && v < s_hi) atomicOr(&selm[v / kChunk], 1u << (v % kChunk));
+    }
+    __syncthreads();
+  } else {
+    // ---- selected indices -> LDS (entries outside [0, Lk) become -1); their
+    // loads were issued before Q's, so only they are waited for here
+#pragma unroll
+    for (int j = 0; j < kIdxPer; ++j) {
+      const int i = c_lo * kChunk + (int)threadIdx.x + j * (int)blockDim.x;
+      if (i < c_hi * kChunk) sidx[i] = (iv[j] >= 0 && iv[j] < a.Lk) ? iv[j] : -1;
+    }
+    __syncthreads();
+    const bool mine = lane >= c_lo && lane < c_hi;
+    bool any = false, all = mine;
+    if (mine)
+      for (int j = 0; j < kChunk; ++j) {
+        const bool v = sidx[lane * kChunk + j] >= 0;
+        any |= v;
+        all &= v;
+      }
+    chunk_mask = __ballot(any);
+    full_mask = __ballot(all);
   }
 
   // ---- gather of one chunk by the first GW waves, BPW 1 KiB blocks each
