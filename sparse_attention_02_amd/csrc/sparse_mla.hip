@@ -208,22 +208,26 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
   } else {
     // ---- selected indices -> LDS (entries outside [0, Lk) become -1); their
     // loads were issued before Q's, so only they are waited for here
+    // A chunk's 32 entries belong to one half of one wave, so two ballots
+    // give the chunk's "some valid" / "all valid" flags; they meet in a byte
+    // per chunk in the last chunk buffer (the first gathers go elsewhere).
+    uint8_t* cflag = kvb + (STAGES - 1) * S::CHUNK_BYTES;
 #pragma unroll
     for (int j = 0; j < kIdxPer; ++j) {
       const int i = c_lo * kChunk + (int)threadIdx.x + j * (int)blockDim.x;
-      if (i < c_hi * kChunk) sidx[i] = (iv[j] >= 0 && iv[j] < a.Lk) ? iv[j] : -1;
+      const bool in = i < c_hi * kChunk;
+      const bool valid = in && iv[j] >= 0 && iv[j] < a.Lk;
+      if (in) sidx[i] = valid ? iv[j] : -1;
+      const uint64_t vb64 = __ballot(valid);
+      const uint32_t half = (uint32_t)(vb64 >> (lane & 32));
+      if ((lane & 31) == 0 && in)
+        cflag[i / kChunk] = (uint8_t)((half != 0u ? 1 : 0) | (half == 0xFFFFFFFFu ? 2 : 0));
     }
     __syncthreads();
     const bool mine = lane >= c_lo && lane < c_hi;
-    bool any = false, all = mine;
-    if (mine)
-      for (int j = 0; j < kChunk; ++j) {
-        const bool v = sidx[lane * kChunk + j] >= 0;
-        any |= v;
-        all &= v;
-      }
-    chunk_mask = __ballot(any);
-    full_mask = __ballot(all);
+    const int fl = mine ? cflag[lane] : 0;
+    chunk_mask = __ballot(fl & 1);
+    full_mask = __ballot(fl & 2);
   }
 
   // ---- gather of one chunk by the first GW waves, BPW 1 KiB blocks each
@@ -508,15 +512,45 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
                                  : a.out + (size_t)row * a.H * DV;
   float* lse_base = a.nsplit > 1 ? a.part_lse + (size_t)vb * a.H
                                  : (a.lse ? a.lse + (size_t)row * a.H : nullptr);
+  // The output rows go out through LDS so that a store instruction writes two
+  // heads x 512 contiguous bytes instead of 16 heads x 64 (the MFMA result
+  // layout).  Each wave stages 8 d-tiles (16 heads x 128 columns, 8 KiB) at a
+  // time in one of the chunk buffers that the last chunk did not use: every
+  // wave passed the last chunk's barrier, so no wave reads them any more and
+  // no gather into them is in flight.  16-byte unit u of head h sits at unit
+  // u ^ h (low 4 bits), so both the writes and the reads are conflict-free.
+  constexpr int kPieceDt = 8;
+  constexpr bool kStaged = S::HTQ == 1 && S::DT % kPieceDt == 0 && STAGES >= 3 &&
+                           (NW / 2) * 16 * kPieceDt * 64 <= S::CHUNK_BYTES;
 #pragma unroll
   for (int ht = 0; ht < S::HTQ; ++ht) {
     float l = l_part[ht] + __shfl_xor(l_part[ht], 16);
     l += __shfl_xor(l, 32);
     const int head = 16 * (S::HTQ * wave + ht) + li;
-    if (head < a.H) {
-      if (g == 0 && lse_base)
-        lse_base[head] = l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if (g == 0 && lse_base && head < a.H)
+      lse_base[head] = l > 0.0f ? (m_use[ht] + fast_log2(l)) * 0.69314718055994530942f : -INFINITY;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    if constexpr (kStaged) {
+      const int last = buf == 0 ? STAGES - 1 : buf - 1;  // buffer of the last chunk
+      int sb = last + 1 + wave / (NW / 2);
+      sb = sb >= STAGES ? sb - STAGES : sb;
+      sb = sb >= STAGES ? sb - STAGES : sb;
+      uint8_t* slot = kvb + sb * S::CHUNK_BYTES + (wave % (NW / 2)) * (16 * kPieceDt * 64);
+      const int hh = lane >> 5, u = lane & 31;
+#pragma unroll
+      for (int pc = 0; pc < S::DT / kPieceDt; ++pc) {
+#pragma unroll
+        for (int j = 0; j < kPieceDt; ++j)
+          *(v4f*)(slot + li * (kPieceDt * 64) + 16 * ((4 * j + g) ^ li)) = acc[ht][kPieceDt * pc + j] * inv;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int h2 = 2 * j + hh;
+          const v4f v = *(const v4f*)(slot + h2 * (kPieceDt * 64) + 16 * (u ^ h2));
+          const int hd = 16 * (S::HTQ * wave + ht) + h2;
+          if (hd < a.H) *(v4f*)(out_base + (size_t)hd * DV + 16 * kPieceDt * pc + 4 * u) = v;
+        }
+      }
+    } else if (head < a.H) {
       float* orow = out_base + (size_t)head * DV;
 #pragma unroll
       for (int dt = 0; dt < S::DT; ++dt) *(v4f*)(orow + 16 * dt + 4 * g) = acc[ht][dt] * inv;
