@@ -50,7 +50,7 @@ def _compare(inp, wl, rows, indices_np, out, lse, label):
 
 
 @pytest.mark.parametrize("name", ["tiny", "ragged", "single_token", "k_above_len", "mla_small",
-                                  "decode_small", "few_queries", "split_prefill"])
+                                  "mla_partial_heads", "decode_small", "few_queries", "split_prefill"])
 def test_masked_mode_matches_oracle(dsa, name):
     wl = dsa_inputs.WORKLOADS[name] if name in dsa_inputs.WORKLOADS else EDGE[name]
     log(f"[{name}] B={wl.batch} Lq={wl.q_len} Lk={wl.kv_len} q_start={wl.q_start} k={wl.topk} "

@@ -81,6 +81,8 @@ EDGE = {
     "decode_small": dsa_inputs.Workload("dec", 15, 3, 1, 1000, 999, 64, 128, 128, 16, 64, 16),
     "few_queries": dsa_inputs.Workload("few", 16, 2, 5, 700, 695, 8, 128, 64, 24, 64, 16),
     "mla_small": dsa_inputs.Workload("mla", 17, 1, 200, 200, 0, 64, 128, 96, 128, 512, 64),
+    # 100 of the 128 head slots: one 16-head tile part-filled, one absent
+    "mla_partial_heads": dsa_inputs.Workload("mlah", 20, 1, 150, 180, 30, 64, 128, 96, 100, 512, 64),
     # long rows that the indexer splits over several blocks (prefill: 4 key
     # ranges of ~20 64-key stages; decode: 8 ranges of ~10 256-key stages),
     # each with a part-filled last stage
