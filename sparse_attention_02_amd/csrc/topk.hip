@@ -13,7 +13,8 @@
 // in index order, the keys above the threshold and the first (needed) keys
 // equal to it.  Rows held in registers are first cut down to a few thousand
 // candidates with a threshold taken from a sample (see select_top).
-//  * Rows of up to 32768 candidates: one block, keys held in registers.
+//  * Rows of up to 32768 candidates: one block, keys held in registers (as
+//    16-bit prefixes, two per register, where the row is 16-byte aligned).
 //  * Longer rows: two stages through a workspace (per-segment top k, then the
 //    top k of the segments' candidates), which also spreads a few long rows
 //    (decode) over many blocks.
@@ -484,6 +485,118 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(TopkArgs a) {
                       [&](uint32_t o, int c, uint32_t) { out[o] = c; });
 }
 
+// Rows of up to EPT * NT candidates with the keys held as 16-bit prefixes
+// (the top half of the order key), two per register: half the registers of
+// the full keys, so three 512-thread blocks fit a CU instead of two.  A cut
+// at a prefix boundary, t << 16, keeps the selection exact (a key is >= t << 16
+// exactly when its prefix is >= t); the exact stage takes the full keys of
+// its at most kCap candidates from the row again (key_at).
+template <int EPT, bool VEC>
+__device__ __forceinline__ void load_prefixes(const float* src, int base, int cnt, uint32_t (&pk)[EPT / 2]) {
+  if (VEC && cnt == EPT) {
+    // every load is issued before any is packed: the row's loads then share
+    // one memory latency (64 registers in flight, then half of them kept)
+    v4f raw[EPT / 4];
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) raw[j] = *(const v4f*)(src + base + 4 * j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      pk[2 * j] = (order_key(raw[j][0]) >> 16) | (order_key(raw[j][1]) & 0xFFFF0000u);
+      pk[2 * j + 1] = (order_key(raw[j][2]) >> 16) | (order_key(raw[j][3]) & 0xFFFF0000u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT; j += 2) {
+      const uint32_t a0 = j < cnt ? order_key(src[base + j]) : 0u;
+      const uint32_t a1 = j + 1 < cnt ? order_key(src[base + j + 1]) : 0u;
+      pk[j / 2] = (a0 >> 16) | (a1 & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int EPT>
+__device__ __forceinline__ uint32_t prefix_at(const uint32_t (&pk)[EPT / 2], int j) {
+  return (j & 1) ? pk[j / 2] >> 16 : pk[j / 2] & 0xFFFFu;
+}
+
+template <int EPT, int NT, typename KeyAt, typename Emit>
+__device__ __forceinline__ void select_top_prefix(BlockSelect<NT> sel, uint32_t (&pk)[EPT / 2], int cnt,
+                                                  int n, uint32_t k, int32_t* ci, KeyAt&& key_at, Emit&& emit) {
+  static_assert(EPT % 16 == 0 && kCap % NT == 0, "sample stride and candidate slots");
+  constexpr int S = EPT / 16;
+  constexpr int E2 = kCap / NT;
+  const int base = EPT * (int)threadIdx.x;
+  uint32_t t = 0;  // a prefix
+  if (n > kCap) {
+    uint32_t smp[S];
+#pragma unroll
+    for (int e = 0; e < S; ++e) smp[e] = prefix_at<EPT>(pk, 16 * e);
+    const int scnt = min(S, (cnt + 15) / 16);
+    const uint32_t m = (uint32_t)(n + 15) / 16;
+    const float qm = (float)k * (float)m / (float)n;
+    const uint32_t r = min(m, (uint32_t)(qm + 4.0f * sqrtf(qm) + 8.0f));
+    t = sel.coarse_threshold(smp, scnt, r);
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) mine += j < cnt && prefix_at<EPT>(pk, j) >= t;
+  uint32_t total;
+  uint32_t o = block_inclusive_scan_n<NT>(mine, sel.scan_sh, total) - mine;
+  const bool filtered = total >= k && total <= (uint32_t)kCap;
+  if (filtered) {
+    // the comparisons are made again rather than kept from the count: 64
+    // live lane masks would not fit the scalar registers
+    asm volatile("" : "+v"(t));
+    int cnt_c = cnt;
+    asm volatile("" : "+v"(cnt_c));
+#pragma unroll
+    for (int i = 0; i < EPT / 2; ++i) asm volatile("" : "+v"(pk[i]));
+#pragma unroll
+    for (int j = 0; j < EPT; ++j)
+      if (j < cnt_c && prefix_at<EPT>(pk, j) >= t) ci[o++] = base + j;
+    __syncthreads();
+    const int b2 = E2 * (int)threadIdx.x;
+    const int cnt2 = max(0, min(E2, (int)total - b2));
+    uint32_t k2[E2];
+#pragma unroll
+    for (int e = 0; e < E2; ++e) k2[e] = e < cnt2 ? key_at(ci[b2 + e]) : 0u;
+    uint32_t T, need, kmin;
+    bool all_ge;
+    sel.threshold(k2, cnt2, k, T, need, all_ge, kmin);
+    sel.emit_top(k2, cnt2, b2, k, T, need, all_ge, kmin,
+                 [&](uint32_t o2, int c2, uint32_t kv) { emit(o2, ci[c2], kv); });
+  } else {
+    select_streamed<NT>(sel.hist, sel.scan_sh, sel.ctrl, key_at, n, k, emit);
+  }
+}
+
+// One block per row of at most EPT * NT candidates, keys as prefixes.
+template <int EPT, bool VEC, int NT>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void topk_prefix_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kHist];
+  __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
+  __shared__ uint32_t ctrl[4];
+  __shared__ int32_t cand_i[kCap];
+  const int row = blockIdx.x;
+  if (a.only_rows && !a.only_rows[row]) return;
+  const int pos = a.q_start + row % a.Lq;
+  const int n = min(pos + 1, a.Lk);
+  int32_t* out = a.indices + (size_t)row * a.k;
+  if (n <= a.k) {
+    for (int i = threadIdx.x; i < a.k; i += NT) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int base = EPT * threadIdx.x;
+  const int cnt = max(0, min(EPT, n - base));
+  const float* srow = a.scores + (size_t)row * a.Lk;
+  uint32_t pk[EPT / 2];
+  load_prefixes<EPT, VEC>(srow, base, cnt, pk);
+  select_top_prefix<EPT, NT>(BlockSelect<NT>{hist, scan_sh, ctrl}, pk, cnt, n, (uint32_t)a.k, cand_i,
+                             [&](int i) { return order_key(srow[i]); },
+                             [&](uint32_t o, int c, uint32_t) { out[o] = c; });
+}
+
 // Rows longer than one block holds are selected in two stages.  The top k of
 // a row are among the union of the top k of its segments (an element beaten
 // by k others inside its segment is beaten by them in the row), and the order
@@ -680,7 +793,7 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
   const int max_n = min(a.q_start + a.Lq, a.Lk);
   if (max_n <= kCandMax) {
     if (a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0)
-      return launch_kernel((const void*)topk_reg_kernel<64, true, 512>, grid, dim3(512), 0, stream, a);
+      return launch_kernel((const void*)topk_prefix_kernel<64, true, 512>, grid, dim3(512), 0, stream, a);
     return launch_kernel((const void*)topk_reg_kernel<64, false, 512>, grid, dim3(512), 0, stream, a);
   }
   const SegPlan plan = topk_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
