@@ -792,9 +792,17 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
   const dim3 grid((unsigned)rows);
   const int max_n = min(a.q_start + a.Lq, a.Lk);
   if (max_n <= kCandMax) {
-    if (a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0)
+    // The prefix form re-reads its candidates' full keys from the row.  With
+    // every row inside the candidate slots that row was just loaded and is
+    // still in L2; longer rows have ~18 % of their keys as candidates, which
+    // touch nearly every cache line of the row after L2 has dropped it (at
+    // L = 32K: 4.2 GB read from the memory side against 2.2 GB for the full
+    // keys, in the same time), so they keep the full keys in registers.
+    const bool vec = a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0;
+    if (vec && max_n <= kCap)
       return launch_kernel((const void*)topk_prefix_kernel<64, true, 512>, grid, dim3(512), 0, stream, a);
-    return launch_kernel((const void*)topk_reg_kernel<64, false, 512>, grid, dim3(512), 0, stream, a);
+    return launch_kernel(vec ? (const void*)topk_reg_kernel<64, true, 512> : (const void*)topk_reg_kernel<64, false, 512>,
+                         grid, dim3(512), 0, stream, a);
   }
   const SegPlan plan = topk_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
   a.nseg = plan.nseg;
