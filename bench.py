@@ -333,41 +333,51 @@ def sclk_probe(launch, n: int):
     amdsmi's current GFX clock, sampled every ~2 ms from a host thread, the
     first and last fifth of the samples dropped.  The published peaks assume
     2.4 GHz; matrix-heavy kernels run below it under load.  None when amdsmi
-    is missing or refuses the query (the figure is informational)."""
+    is missing, refuses the query or does not answer within a few seconds
+    (the figure is informational; the sampling thread is a daemon, so a
+    query that never returns cannot hold the bench)."""
     import threading
     import torch
-    try:
-        import amdsmi
-        amdsmi.amdsmi_init()
-        handle = amdsmi.amdsmi_get_processor_handles()[0]
-        amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)
-    except Exception:
-        return None
     samples = []
+    ready = threading.Event()
     stop = threading.Event()
 
     def poll():
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handle = amdsmi.amdsmi_get_processor_handles()[0]
+            gfx = amdsmi.AmdSmiClkType.GFX
+            amdsmi.amdsmi_get_clock_info(handle, gfx)
+        except Exception:
+            ready.set()
+            return
+        ready.set()
         while not stop.is_set():
             try:
-                samples.append(float(amdsmi.amdsmi_get_clock_info(handle, amdsmi.AmdSmiClkType.GFX)["clk"]))
+                samples.append(float(amdsmi.amdsmi_get_clock_info(handle, gfx)["clk"]))
             except Exception:
                 pass
             time.sleep(0.002)
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
 
-    torch.cuda.synchronize()
-    for _ in range(n):
-        launch()
     th = threading.Thread(target=poll, daemon=True)
     th.start()
+    if not ready.wait(5.0):
+        return None
+    torch.cuda.synchronize()
+    samples.clear()
+    for _ in range(n):
+        launch()
     torch.cuda.synchronize()
     stop.set()
-    th.join()
-    try:
-        amdsmi.amdsmi_shut_down()
-    except Exception:
-        pass
-    cut = len(samples) // 5
-    mid = samples[cut:len(samples) - cut] or samples
+    th.join(5.0)
+    got = list(samples)
+    cut = len(got) // 5
+    mid = got[cut:len(got) - cut] or got
     return float(sum(mid) / len(mid)) / 1e3 if mid else None
 
 
