@@ -328,59 +328,6 @@ def traffic_for(kernel: str):
     return e.get("hbm_bytes_per_launch")
 
 
-def sclk_probe(launch, n: int):
-    """Shader clock (GHz) while `launch` runs n times back to back on the GPU:
-    amdsmi's current GFX clock, sampled every ~2 ms from a host thread, the
-    first and last fifth of the samples dropped.  The published peaks assume
-    2.4 GHz; matrix-heavy kernels run below it under load.  None when amdsmi
-    is missing, refuses the query or does not answer within a few seconds
-    (the figure is informational; the sampling thread is a daemon, so a
-    query that never returns cannot hold the bench)."""
-    import threading
-    import torch
-    samples = []
-    ready = threading.Event()
-    stop = threading.Event()
-
-    def poll():
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handle = amdsmi.amdsmi_get_processor_handles()[0]
-            gfx = amdsmi.AmdSmiClkType.GFX
-            amdsmi.amdsmi_get_clock_info(handle, gfx)
-        except Exception:
-            ready.set()
-            return
-        ready.set()
-        while not stop.is_set():
-            try:
-                samples.append(float(amdsmi.amdsmi_get_clock_info(handle, gfx)["clk"]))
-            except Exception:
-                pass
-            time.sleep(0.002)
-        try:
-            amdsmi.amdsmi_shut_down()
-        except Exception:
-            pass
-
-    th = threading.Thread(target=poll, daemon=True)
-    th.start()
-    if not ready.wait(5.0):
-        return None
-    torch.cuda.synchronize()
-    samples.clear()
-    for _ in range(n):
-        launch()
-    torch.cuda.synchronize()
-    stop.set()
-    th.join(5.0)
-    got = list(samples)
-    cut = len(got) // 5
-    mid = got[cut:len(got) - cut] or got
-    return float(sum(mid) / len(mid)) / 1e3 if mid else None
-
-
 def cpu_baseline(wl, target_s: float):
     """The oracle (as it stands) on an evenly spaced row sample of the workload."""
     import numpy as np
@@ -601,21 +548,6 @@ def main():
         k.update(algorithmic_gbs=gbs, frac_of_hbm_peak=gbs / PEAK_HBM_GBS)
         kernels[n] = k
 
-    # shader clock under each matrix kernel's own load, and the fraction of
-    # peak at that clock
-    clk_runs = {"index_scores": (lambda: dsa.dsa_index_scores(prob, q_idx, k_idx, w, scores, stream=stream),
-                                 max(4, int(150.0 / max(kernels["index_scores"]["avg_ms"], 1e-3)))),
-                attn_name: ((lambda: dsa.dsa_sparse_mla_attn_ws(prob, q, kv, indices, out, lse, aws, aws_bytes,
-                                                                stream=stream)) if args.attn == "sparse" else
-                            (lambda: dsa.dsa_masked_mha_attn(prob, q, kv, indices, out, lse, stream=stream)),
-                            max(4, int(150.0 / max(kernels[attn_name]["avg_ms"], 1e-3))))}
-    for n, (fn, reps) in clk_runs.items():
-        if "frac_of_mfma_peak" not in kernels[n]:
-            continue
-        ghz = sclk_probe(fn, reps)
-        kernels[n]["sclk_ghz"] = ghz
-        kernels[n]["frac_of_mfma_peak_at_sclk"] = (kernels[n]["frac_of_mfma_peak"] * 2.4 / ghz) if ghz else None
-
     # the step's selection call: the indexer's roofline, plus the top-k's
     # score read when the scores are written out
     sel_roof = kernels["index_scores"]["roofline_ms"] + (0.0 if sampled else kernels["topk"]["roofline_ms"])
@@ -664,8 +596,6 @@ def main():
         "indexer_fp8_tflops": kernels["index_scores"]["tflops"],
         "indexer_frac_of_fp8_peak": kernels["index_scores"]["frac_of_mfma_peak"],
         "indexer_fp8_tflops_median": work["index_scores"]["flop"] / (kernels["index_scores"]["median_ms"] * 1e-3) / 1e12,
-        "indexer_sclk_ghz": kernels["index_scores"].get("sclk_ghz"),
-        "indexer_frac_of_fp8_peak_at_sclk": kernels["index_scores"].get("frac_of_mfma_peak_at_sclk"),
         "kernels": kernels,
         "cpu_baseline": None,
     }
