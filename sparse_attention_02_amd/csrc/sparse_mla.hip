@@ -561,25 +561,36 @@ __global__ __launch_bounds__(64 * NW) void sparse_mla_kernel(AttnArgs a) {
 // Merge of the parts of split rows: lse = log(sum_p exp(lse_p)) and
 // out = sum_p exp(lse_p - lse) * out_p (each part is normalised by its own
 // softmax sum); a row without any valid entry keeps out = 0, lse = -inf.
-// One block per (row, head), one 4-column group per thread.
+// One block per (row, head), one 4-column group per thread.  Every part's
+// lse and columns are loaded before any is used, so a thread waits for one
+// memory latency instead of two (the lse, then the columns it weighs).
+constexpr int kMaxParts = 8;  // attn_splits never splits a row further
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int rh = blockIdx.x;  // row * H + head
   const int row = rh / a.H, head = rh % a.H;
-  const float* lp = a.part_lse + (size_t)row * a.nsplit * a.H + head;
-  float m = -INFINITY;
-  for (int p = 0; p < a.nsplit; ++p) m = fmaxf(m, lp[(size_t)p * a.H]);
-  float sum = 0.0f;
-  for (int p = 0; p < a.nsplit; ++p) sum += m == -INFINITY ? 0.0f : __expf(lp[(size_t)p * a.H] - m);
-  const float lse = sum > 0.0f ? m + __logf(sum) : -INFINITY;
-  if (threadIdx.x == 0 && a.lse) a.lse[rh] = lse;
+  const int np = a.nsplit;
+  const float* lp = a.part_lse + (size_t)row * np * a.H + head;
+  const float* op = a.part_out + ((size_t)row * np * a.H + head) * a.Dv;
   for (int d4 = threadIdx.x; d4 < a.Dv / 4; d4 += blockDim.x) {
-    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int p = 0; p < a.nsplit; ++p) {
-      const float lpp = lp[(size_t)p * a.H];
-      if (lpp == -INFINITY) continue;
-      const float wgt = __expf(lpp - lse);
-      o += wgt * *(const v4f*)(a.part_out + (((size_t)row * a.nsplit + p) * a.H + head) * a.Dv + 4 * d4);
+    float lv[kMaxParts];
+    v4f ov[kMaxParts];
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p) {
+      lv[p] = p < np ? lp[(size_t)p * a.H] : -INFINITY;
+      ov[p] = p < np ? *(const v4f*)(op + (size_t)p * a.H * a.Dv + 4 * d4) : (v4f){0.0f, 0.0f, 0.0f, 0.0f};
     }
+    float m = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p) m = fmaxf(m, lv[p]);
+    float sum = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p) sum += (p < np && m != -INFINITY) ? __expf(lv[p] - m) : 0.0f;
+    const float lse = sum > 0.0f ? m + __logf(sum) : -INFINITY;
+    if (d4 == 0 && a.lse) a.lse[rh] = lse;
+    v4f o = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int p = 0; p < kMaxParts; ++p)
+      if (p < np && lv[p] != -INFINITY) o += __expf(lv[p] - lse) * ov[p];
     *(v4f*)(a.out + (size_t)rh * a.Dv + 4 * d4) = o;
   }
 }
@@ -596,6 +607,7 @@ hipError_t launch_stages(const AttnArgs& a, size_t smem, hipStream_t stream) {
 template <int DQK, int DV, int NW, bool MASKED>
 hipError_t launch_shape(const AttnArgs& a, hipStream_t stream) {
   using S = AttnShape<DQK, DV, NW>;
+  if (a.nsplit < 1 || a.nsplit > kMaxParts) return hipErrorInvalidValue;  // the merge holds 8 parts
   // sparse: the staged indices; masked: one selection word per chunk of the row
   const size_t tail = MASKED ? (size_t)((a.Lk + kChunk - 1) / kChunk) * sizeof(uint32_t)
                              : (size_t)((a.k + kChunk - 1) / kChunk) * kChunk * sizeof(int32_t);
