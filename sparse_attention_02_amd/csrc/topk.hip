@@ -388,21 +388,44 @@ struct BlockSelect {
 template <int EPT, int NT, typename KeyAt, typename Emit>
 __device__ __forceinline__ void select_top(BlockSelect<NT> sel, uint32_t (&key)[EPT], int cnt, int n,
                                            uint32_t k, uint32_t* ck, int32_t* ci, KeyAt&& key_at,
-                                           Emit&& emit) {
+                                           Emit&& emit, int n_real = -1) {
   static_assert(EPT % 16 == 0 && kCap % NT == 0, "sample stride and candidate slots");
   constexpr int S = EPT / 16;     // samples per thread: candidates 16s of its range
   constexpr int E2 = kCap / NT;   // candidates per thread in the exact selection
   const int base = EPT * (int)threadIdx.x;
-  uint32_t t = 0;  // every key is >= 0
-  if (n > kCap) {
+  // n_real >= 0: the n slots hold n_real real keys (>= 1) among padding
+  // keys 0; the cut then never lets the padding through, and the sample's
+  // size and rank are taken over the real keys it holds
+  const bool padded = n_real >= 0;
+  const int nr = padded ? n_real : n;
+  uint32_t t = padded ? 1u : 0u;  // every (real) key is >= t
+  if (nr > kCap) {
     uint32_t smp[S];
 #pragma unroll
     for (int e = 0; e < S; ++e) smp[e] = key[16 * e];
     const int scnt = min(S, (cnt + 15) / 16);
-    const uint32_t m = (uint32_t)(n + 15) / 16;  // sampled candidates: 0, 16, 32, ... < n
-    const float qm = (float)k * (float)m / (float)n;
+    uint32_t m = (uint32_t)(n + 15) / 16;  // sampled candidates: 0, 16, 32, ... < n
+    if (padded) {
+      // padding samples take the smallest real sample's value, so that the
+      // cut's digits span the real keys only (from 0 they would crowd them
+      // into a few coarse bins); they still rank below every real sample
+      uint32_t real = 0, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+      for (int e = 0; e < S; ++e)
+        if (e < scnt && smp[e] != 0u) {
+          lo = min(lo, smp[e]);
+          ++real;
+        }
+      block_minmax<NT>(lo, hi, sel.scan_sh);
+#pragma unroll
+      for (int e = 0; e < S; ++e) smp[e] = smp[e] != 0u ? smp[e] : lo;
+      block_inclusive_scan_n<NT>(real, sel.scan_sh, m);
+      m = max(m, 1u);
+    }
+    const float qm = (float)k * (float)m / (float)nr;
     const uint32_t r = min(m, (uint32_t)(qm + 4.0f * sqrtf(qm) + 8.0f));
     t = sel.coarse_threshold(smp, scnt, r);
+    if (padded) t = max(t, 1u);
   }
   // One scan of the per-thread counts of keys >= t gives both the total (is
   // the cut usable: at least k and at most kCap candidates) and each
@@ -683,6 +706,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t
     if (flags && threadIdx.x == 0) flags[row] = 0;
     return;
   }
+  int n_real = -1;  // with counts: the real candidates among the slots
   if (row_count) {
     if (threadIdx.x < 64) {
       int found = 0, over = 0;
@@ -693,10 +717,14 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t
       }
       found = (int)wave_scan_add((uint32_t)found);
       over = __ballot(over) != 0;
-      if (threadIdx.x == 63) ctrl[3] = (over || found < a.k) ? 1u : 0u;
+      if (threadIdx.x == 63) {
+        ctrl[3] = (over || found < a.k) ? 1u : 0u;
+        ctrl[2] = (uint32_t)found;
+      }
     }
     __syncthreads();
     const bool bad = ctrl[3] != 0;
+    n_real = (int)ctrl[2];
     __syncthreads();
     if (threadIdx.x == 0) flags[row] = bad ? 1 : 0;
     if (bad) return;
@@ -720,7 +748,7 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t
   }
   select_top<EPT, NT>(BlockSelect<NT>{hist, scan_sh, ctrl}, key, cnt, n, (uint32_t)a.k, cand_k, cand_i,
                       [&](int i) { return ck[i]; },
-                      [&](uint32_t o, int c, uint32_t) { out[o] = ci[c]; });
+                      [&](uint32_t o, int c, uint32_t) { out[o] = ci[c]; }, n_real);
 }
 
 // Segment plan of the two-stage path: nseg segments of kSeg keys (wide =
@@ -779,11 +807,148 @@ __global__ __launch_bounds__(NT) void fused_threshold_kernel(const float* sample
   if (threadIdx.x == 0) thresh[row] = t;
 }
 
+// ---- Few long rows (decode): a sampled cut, a filter, and one exact select.
+// The two-stage path spends most of its time in per-segment selections that
+// keep a quarter of each segment; with few rows the chip is better used by
+// (1) one block per row that takes a cut from a sample of the row, (2) a
+// filter over every key that keeps those at or above the cut, in index
+// order, into fixed slots per split of the row, and (3) the candidate select
+// above (topk_cand_kernel with counts and flags), which checks the row and
+// selects exactly.  A row whose split overflowed its slots, or that kept
+// fewer than k keys, is flagged and redone by the two-stage path restricted
+// to the flagged rows.  Exactness as for the fused selection: when at least
+// k keys are >= t and all of them were kept, the k-th largest is >= t, so
+// every selectable key (ties included) is a candidate, in index order.
+constexpr int kRunLen = 64;       // sample: the first 64 keys of every 1024 (or more:
+constexpr int kRunStride = 1024;  // the stride doubles until the sample fits the block)
+constexpr int kCutSamples = 16 * 512;
+__host__ __device__ inline int run_stride(int n) {
+  int rs = kRunStride;
+  while ((long long)((n + rs - 1) / rs) * kRunLen > kCutSamples) rs *= 2;
+  return rs;
+}
+constexpr int kFiltSplit = 4096;  // keys per split of the filter (256 threads x 16)
+constexpr int kFewRows = 256;
+
+// Cut of one row from its sample (the keys rs j .. rs j + 63 below the row's
+// length, read as 256-byte runs, rs = 1024 or the least power-of-two multiple
+// that keeps the sample within the block), with the same rank rule as
+// select_top's own sample; written as an order key.
+template <int EPT, int NT>
+__global__ __launch_bounds__(NT) void topk_sample_cut_kernel(TopkArgs a, uint32_t* thresh) {
+  static_assert(EPT * NT == kCutSamples, "sample size");
+  __shared__ uint32_t hist[kHist];
+  __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
+  __shared__ uint32_t ctrl[4];
+  const int row = blockIdx.x;
+  const int pos = a.q_start + row % a.Lq;
+  const int n = min(pos + 1, a.Lk);
+  if (n <= a.k) {
+    if (threadIdx.x == 0) thresh[row] = 0u;
+    return;
+  }
+  const int rs = run_stride(n);
+  const int full_runs = n / rs, tail = min(kRunLen, n - full_runs * rs);
+  const int m = full_runs * kRunLen + tail;  // sampled keys, <= EPT * NT
+  const float* src = a.scores + (size_t)row * a.Lk;
+  const int tid = threadIdx.x;
+  // sample s = j * NT + tid is key (s / 64) * rs + s % 64; those below m
+  // are a prefix of the thread's slots
+  const int cnt = tid < m ? min(EPT, (m - tid + NT - 1) / NT) : 0;
+  uint32_t key[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int sidx = j * NT + tid;
+    key[j] = j < cnt ? order_key(src[(sidx / kRunLen) * rs + sidx % kRunLen]) : 0u;
+  }
+  const float qm = (float)a.k * (float)m / (float)n;
+  const uint32_t r = min((uint32_t)m, (uint32_t)(qm + 4.0f * sqrtf(qm) + 8.0f));
+  BlockSelect<NT> sel{hist, scan_sh, ctrl};
+  const uint32_t t = sel.coarse_threshold(key, cnt, r);
+  if (threadIdx.x == 0) thresh[row] = t;
+}
+
+// The keys >= the row's cut of one split (kFiltSplit keys, EPT per thread,
+// contiguous), as (order key, index) in index order into the split's
+// a.seg_cap slots; the rest of the slots are padded (key 0 below every kept
+// key, which are stored as >= 1, index -1).  The split's count may exceed
+// its slots; the select kernel then flags the row.
+template <int EPT, int NT, bool VEC>
+__global__ __launch_bounds__(NT) void topk_filter_kernel(TopkArgs a, const uint32_t* thresh, int32_t* row_count) {
+  static_assert(EPT * NT == kFiltSplit, "one split per block");
+  __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
+  const int row = blockIdx.x / a.nseg, split = blockIdx.x % a.nseg;
+  const int pos = a.q_start + row % a.Lq;
+  const int n_row = min(pos + 1, a.Lk);
+  const size_t slot0 = ((size_t)row * a.nseg + split) * a.seg_cap;
+  uint32_t* ck = a.cand_key + slot0;
+  int32_t* ci = a.cand_idx + slot0;
+  const uint32_t t = thresh[row];
+  const int base = split * kFiltSplit + EPT * (int)threadIdx.x;
+  const int cnt = max(0, min(EPT, n_row - base));
+  uint32_t key[EPT];
+  load_keys<EPT, VEC>(a.scores + (size_t)row * a.Lk, base, cnt, key);
+  uint32_t mine = 0;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) mine += j < cnt && key[j] >= t;
+  uint32_t total;
+  uint32_t o = block_inclusive_scan_n<NT>(mine, scan_sh, total) - mine;
+#pragma unroll
+  for (int j = 0; j < EPT; ++j)
+    if (j < cnt && key[j] >= t) {
+      if (o < (uint32_t)a.seg_cap) {
+        ck[o] = max(key[j], 1u);
+        ci[o] = base + j;
+      }
+      ++o;
+    }
+  for (int i = (int)min(total, (uint32_t)a.seg_cap) + (int)threadIdx.x; i < a.seg_cap; i += NT) {
+    ck[i] = 0u;
+    ci[i] = -1;
+  }
+  if (threadIdx.x == 0) row_count[(size_t)row * a.nseg + split] = (int32_t)total;
+}
+
+// Plan of the few-rows path (use = false where it does not apply).
+struct CutPlan {
+  bool use;
+  int nsplit;  // filter splits per row
+  int cap;     // candidate slots per split
+};
+CutPlan cut_plan(long long rows, int Lq, int q_start, int Lk, int k) {
+  const int max_n = min(q_start + Lq, Lk);
+  if (rows > kFewRows || max_n <= kCandMax || k % 4 != 0) return {false, 0, 0};
+  // expected keys >= the cut in the longest row: r samples scaled by n / m
+  const int rs = run_stride(max_n);
+  const int runs = max_n / rs, tail = min(kRunLen, max_n - runs * rs);
+  const double m = (double)runs * kRunLen + tail;
+  const double qm = (double)k * m / max_n;
+  const double expect = (qm + 4.0 * sqrt(qm) + 8.0) * max_n / m;
+  const int nsplit = (max_n + kFiltSplit - 1) / kFiltSplit;
+  int cap = 64;
+  while (cap < 2.0 * expect / nsplit + 64.0) cap *= 2;
+  if ((long long)nsplit * cap > kCandMax) return {false, 0, 0};
+  return {true, nsplit, cap};
+}
+
 }  // namespace
 
+// Few-rows path: row flags (rounded to 256 bytes), then one region holding
+// either its cuts, counts and candidates or, for the flagged rows, the
+// two-stage path's candidates.
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+static size_t cut_region_bytes(long long rows, const CutPlan& c) {
+  return round256((size_t)rows * sizeof(uint32_t)) + round256((size_t)rows * c.nsplit * sizeof(int32_t)) +
+         (size_t)rows * c.nsplit * c.cap * (sizeof(uint32_t) + sizeof(int32_t));
+}
+
 size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k) {
-  const int nseg = topk_plan((long long)B * Lq, Lq, q_start, Lk, k).nseg;
-  return (size_t)B * Lq * nseg * k * (sizeof(uint32_t) + sizeof(int32_t));
+  const long long rows = (long long)B * Lq;
+  const int nseg = topk_plan(rows, Lq, q_start, Lk, k).nseg;
+  const size_t two_stage = (size_t)rows * nseg * k * (sizeof(uint32_t) + sizeof(int32_t));
+  const CutPlan c = cut_plan(rows, Lq, q_start, Lk, k);
+  if (!c.use || nseg == 0) return two_stage;
+  return round256((size_t)rows * sizeof(int32_t)) + std::max(two_stage, cut_region_bytes(rows, c));
 }
 
 hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
@@ -805,6 +970,34 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
                          grid, dim3(512), 0, stream, a);
   }
   const SegPlan plan = topk_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
+  const CutPlan cut = cut_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
+  int32_t* flags = nullptr;
+  if (cut.use && plan.nseg > 0 && a.workspace && !a.only_rows) {
+    // few long rows: cut, filter, exact select; flagged rows go on below
+    uint8_t* ws = (uint8_t*)a.workspace;
+    flags = (int32_t*)ws;
+    uint8_t* region = ws + round256((size_t)rows * sizeof(int32_t));
+    uint32_t* thresh = (uint32_t*)region;
+    int32_t* count = (int32_t*)(region + round256((size_t)rows * sizeof(uint32_t)));
+    TopkArgs c = a;
+    c.nseg = cut.nsplit;
+    c.seg_cap = cut.cap;
+    c.cand_key = (uint32_t*)((uint8_t*)count + round256((size_t)rows * cut.nsplit * sizeof(int32_t)));
+    c.cand_idx = (int32_t*)(c.cand_key + (size_t)rows * cut.nsplit * cut.cap);
+    const bool vec = a.Lk % 4 == 0 && (uintptr_t)a.scores % 16 == 0;
+    hipError_t e = launch_kernel((const void*)topk_sample_cut_kernel<kCutSamples / 512, 512>, grid, dim3(512), 0, stream, c, thresh);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(vec ? (const void*)topk_filter_kernel<16, 256, true> : (const void*)topk_filter_kernel<16, 256, false>,
+                      dim3((unsigned)(rows * cut.nsplit)), dim3(256), 0, stream, c, (const uint32_t*)thresh,
+                      count);
+    if (e != hipSuccess) return e;
+    e = launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, c, (const int32_t*)count,
+                      flags);
+    if (e != hipSuccess) return e;
+    // the two-stage path below, for the flagged rows only, in the same region
+    a.workspace = region;
+    a.only_rows = flags;
+  }
   a.nseg = plan.nseg;
   if (a.nseg > 0 && a.workspace) {
     a.seg_cap = a.k;

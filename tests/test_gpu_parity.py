@@ -175,6 +175,42 @@ def test_topk_two_stage_long_rows(dsa, k, Lk, Lq):
     np.testing.assert_array_equal(got[1, -1], np.arange(k))
 
 
+@pytest.mark.parametrize("Lk", [131072, 40001])
+def test_topk_few_rows_cut_and_flagged_rows(dsa, Lk):
+    """Few long rows are first selected from a cut taken on a sample of each
+    row (the first 64 keys of every 1024): the keys at or above it are kept
+    in 4096-key splits and selected exactly, and a row the cut cannot settle
+    is flagged and redone in two stages.  Row 0 is random (settled by the
+    cut); in row 1 the sampled keys are the row's lowest, so the cut lets
+    nearly every key through and the splits overflow; in row 2 they are its
+    highest, so fewer than k keys pass; row 3 is all equal.  Lk = 40001 also
+    takes the scalar loads and a partial last run."""
+    rng = np.random.default_rng(Lk)
+    k, B, Lq = 2048, 4, 1
+    q_start = Lk - 1
+    wl = dsa_inputs.Workload("few", 0, B, Lq, Lk, q_start, 4, 32, k, 8, 64, 16)
+    s = (rng.standard_normal((B, Lq, Lk)) * 100.0).astype(np.float32)
+    sampled = (np.arange(Lk) % 1024) < 64
+    ns = int(sampled.sum())
+    s[1, 0, sampled] = (-1000.0 + rng.standard_normal(ns)).astype(np.float32)
+    s[2, 0, sampled] = (1000.0 + rng.standard_normal(ns)).astype(np.float32)
+    s[2, 0, ~sampled] = rng.standard_normal(Lk - ns).astype(np.float32)
+    s[3] = 5.0
+    prob = dsa.Problem.from_workload(wl)
+    ws_bytes = dsa.workspace_size(prob, dsa.DSA_OP_TOPK)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    idx = torch.full((B, Lq, k), -7, dtype=torch.int32, device="cuda")
+    log(f"[few rows] Lk={Lk} k={k} rows={B * Lq} workspace {ws_bytes} bytes")
+    dsa.dsa_topk(prob, dev(s), idx, ws, ws_bytes)
+    torch.cuda.synchronize()
+    pos = (q_start + np.arange(Lq)).astype(np.int32)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        ref = oracle.topk(np.ascontiguousarray(s[b]), pos, k)
+        np.testing.assert_array_equal(got[b], ref)
+    np.testing.assert_array_equal(got[3, 0], np.arange(k))
+
+
 def test_topk_two_stage_needs_workspace(dsa):
     wl = dsa_inputs.Workload("long", 0, 1, 2, 40000, 39998, 4, 32, 64, 8, 64, 16)
     prob = dsa.Problem.from_workload(wl)
