@@ -143,15 +143,16 @@ int dsa_index_scores(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* 
  *              Segments hold 32768 keys while nseg*k <= 65536 (rows of up to
  *              1,048,576 candidates at k = 2048); 8192 keys instead when
  *              nseg*k <= 32768 for them and B*Lq times the 32768-key segment
- *              count is below 2048 (few rows, as in decode).  With at most
- *              256 rows (and k % 4 == 0) the workspace also starts with B*Lq*4
- *              bytes of row flags, rounded up to 256: such rows are first
- *              selected from a cut taken on a 1/16 sample of the row (keys at
- *              or above it kept in 4096-key splits, then one exact select);
- *              a row the cut does not settle is flagged and redone in two
- *              stages.  Longer rows need no workspace: they are selected by
- *              passes that re-read the row.  Contents on return are
- *              unspecified.
+ *              count is below 2048.  At most 256 such rows (k % 4 == 0, as
+ *              in decode) are selected instead from a cut taken on a 1/16
+ *              sample of each row: the keys at or above it are kept in
+ *              4096-key splits of a few hundred slots each, then selected
+ *              exactly (a row the cut does not settle is selected from its
+ *              scores by passes over the row); the workspace then holds a
+ *              cut per row, a count per split and the splits' slots (about
+ *              4 MB for 64 rows of 131072 keys).  Longer rows need no
+ *              workspace: they are selected by passes that re-read the
+ *              row.  Contents on return are unspecified.
  */
 int dsa_topk(const dsa_problem* p, const float* scores, int32_t* indices, void* workspace,
              size_t workspace_bytes, void* stream);

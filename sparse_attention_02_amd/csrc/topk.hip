@@ -689,7 +689,14 @@ __global__ __launch_bounds__(NT) void topk_seg_kernel(TopkArgs a) {
 // its candidates within its slots and at least k were found; otherwise it is
 // flagged (flags[row] = 1) for the plain path.  Every row gets its flag.
 template <int NT>
-__global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t* row_count, int32_t* flags) {
+// With counts (row_count): a row whose split overflowed its slots, or that
+// kept fewer than k keys, is flagged (flags[row] = 1, when flags is given)
+// and left to the caller; with stream_scores (the rows' stored scores) the
+// block selects such a row itself, by passes over the row.  Every launch
+// passes all four arguments (launches through argument pointers do not
+// apply defaults).
+__global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t* row_count, int32_t* flags,
+                                                       const float* stream_scores) {
   constexpr int EPT = 64;
   __shared__ uint32_t hist[kHist];
   __shared__ uint32_t scan_sh[2 * (NT / 64) + 1];
@@ -726,8 +733,15 @@ __global__ __launch_bounds__(NT) void topk_cand_kernel(TopkArgs a, const int32_t
     const bool bad = ctrl[3] != 0;
     n_real = (int)ctrl[2];
     __syncthreads();
-    if (threadIdx.x == 0) flags[row] = bad ? 1 : 0;
-    if (bad) return;
+    if (flags && threadIdx.x == 0) flags[row] = bad ? 1 : 0;
+    if (bad) {
+      if (stream_scores) {
+        const float* srow = stream_scores + (size_t)row * a.Lk;
+        select_streamed<NT>(hist, scan_sh, ctrl, [&](int i) { return order_key(srow[i]); }, n_row,
+                            (uint32_t)a.k, [&](uint32_t o, int c, uint32_t) { out[o] = c; });
+      }
+      return;
+    }
   }
   const int n = a.nseg * a.seg_cap;
   const uint32_t* ck = a.cand_key + (size_t)row * n;
@@ -933,9 +947,8 @@ CutPlan cut_plan(long long rows, int Lq, int q_start, int Lk, int k) {
 
 }  // namespace
 
-// Few-rows path: row flags (rounded to 256 bytes), then one region holding
-// either its cuts, counts and candidates or, for the flagged rows, the
-// two-stage path's candidates.
+// Few-rows path: the cuts and the split counts (each rounded to 256 bytes),
+// then the splits' candidate slots.
 static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
 static size_t cut_region_bytes(long long rows, const CutPlan& c) {
   return round256((size_t)rows * sizeof(uint32_t)) + round256((size_t)rows * c.nsplit * sizeof(int32_t)) +
@@ -948,7 +961,7 @@ size_t topk_workspace_bytes(int B, int Lq, int q_start, int Lk, int k) {
   const size_t two_stage = (size_t)rows * nseg * k * (sizeof(uint32_t) + sizeof(int32_t));
   const CutPlan c = cut_plan(rows, Lq, q_start, Lk, k);
   if (!c.use || nseg == 0) return two_stage;
-  return round256((size_t)rows * sizeof(int32_t)) + std::max(two_stage, cut_region_bytes(rows, c));
+  return cut_region_bytes(rows, c);
 }
 
 hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
@@ -971,12 +984,10 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
   }
   const SegPlan plan = topk_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
   const CutPlan cut = cut_plan(rows, a.Lq, a.q_start, a.Lk, a.k);
-  int32_t* flags = nullptr;
   if (cut.use && plan.nseg > 0 && a.workspace && !a.only_rows) {
-    // few long rows: cut, filter, exact select; flagged rows go on below
-    uint8_t* ws = (uint8_t*)a.workspace;
-    flags = (int32_t*)ws;
-    uint8_t* region = ws + round256((size_t)rows * sizeof(int32_t));
+    // few long rows: cut, filter, exact select (a row the cut does not
+    // settle is selected by the same block from its stored scores)
+    uint8_t* region = (uint8_t*)a.workspace;
     uint32_t* thresh = (uint32_t*)region;
     int32_t* count = (int32_t*)(region + round256((size_t)rows * sizeof(uint32_t)));
     TopkArgs c = a;
@@ -991,12 +1002,9 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
                       dim3((unsigned)(rows * cut.nsplit)), dim3(256), 0, stream, c, (const uint32_t*)thresh,
                       count);
     if (e != hipSuccess) return e;
-    e = launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, c, (const int32_t*)count,
-                      flags);
-    if (e != hipSuccess) return e;
-    // the two-stage path below, for the flagged rows only, in the same region
-    a.workspace = region;
-    a.only_rows = flags;
+    int32_t* no_flags = nullptr;
+    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, c, (const int32_t*)count,
+                         no_flags, a.scores);
   }
   a.nseg = plan.nseg;
   if (a.nseg > 0 && a.workspace) {
@@ -1015,9 +1023,12 @@ hipError_t launch_topk(const TopkArgs& args, hipStream_t stream) {
     if (e != hipSuccess) return e;
     const int32_t* no_count = nullptr;
     int32_t* no_flags = nullptr;
+    const float* no_scores = nullptr;
     if ((long long)a.nseg * a.k > kCandMax)
-      return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a, no_count, no_flags);
-    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a, no_count, no_flags);
+      return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a, no_count, no_flags,
+                           no_scores);
+    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a, no_count, no_flags,
+                         no_scores);
   }
   const size_t base = (size_t)(kBins + kWaves + 1 + 4) * sizeof(uint32_t);
   return launch_kernel((const void*)topk_kernel, grid, dim3(kThreads), base, stream, a);
@@ -1072,11 +1083,14 @@ hipError_t launch_fused_threshold(const float* sample, uint32_t* thresh, int B, 
 
 hipError_t launch_fused_select(const TopkArgs& a, const int32_t* row_count, int32_t* flags, hipStream_t stream) {
   const dim3 grid((unsigned)((long long)a.B * a.Lq));
+  const float* no_scores = nullptr;  // flagged rows go back to the caller
   const long long n = (long long)a.nseg * a.seg_cap;
   if (n <= kCandMax)
-    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a, row_count, flags);
+    return launch_kernel((const void*)topk_cand_kernel<512>, grid, dim3(512), 0, stream, a, row_count, flags,
+                         no_scores);
   if (n <= kCandWide)
-    return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a, row_count, flags);
+    return launch_kernel((const void*)topk_cand_kernel<1024>, grid, dim3(1024), 0, stream, a, row_count, flags,
+                         no_scores);
   return hipErrorInvalidValue;
 }
 

@@ -237,18 +237,23 @@ def test_workspace_sizes_and_forward_checks():
     assert dsa.workspace_size(GOOD, dsa.DSA_OP_SPARSE_MLA_ATTN) == 0
     # few long rows: the top-k splits rows into segments, the attention splits
     # each row's entries over blocks; both need scratch
-    # (few rows: 256 bytes of row flags in front of the candidates, for the
-    # rows the sampled cut leaves to the two-stage path)
+    # (few rows: a cut per row and a count per 4096-key split, each rounded
+    # to 256 bytes, then the splits' slots: 32 splits x 256 slots at 131K,
+    # the slots a power of two >= 2 x 2900 expected keys / 32 + 64)
     dec = Problem(64, 1, 131072, 131071, 64, 128, 2048, 128, 512, 64)
-    assert dsa.workspace_size(dec, dsa.DSA_OP_TOPK) == 256 + 64 * 16 * 2048 * 8
+    assert dsa.workspace_size(dec, dsa.DSA_OP_TOPK) == 256 + 64 * 32 * 4 + 64 * 32 * 256 * 8
     assert dsa.workspace_size(dec, dsa.DSA_OP_SPARSE_MLA_ATTN) == 64 * 4 * 128 * 513 * 4
     # many long rows (chunked prefill): 32K-key segments, 4 per 131K row
     chunk = Problem(1, 8192, 131072, 122880, 64, 128, 2048, 128, 512, 64)
     assert dsa.workspace_size(chunk, dsa.DSA_OP_TOPK) == 8192 * 4 * 2048 * 8
     assert dsa.workspace_size(chunk, dsa.DSA_OP_SPARSE_MLA_ATTN) == 0
-    # 1M-key rows take 32 such segments whatever the row count
+    # four 1M-key rows: 256 splits of 128 slots (the sample takes every
+    # 8192nd run, 5120 keys expected above the cut)
     m1 = Problem(4, 1, 1048576, 1048575, 64, 128, 2048, 128, 512, 64)
-    assert dsa.workspace_size(m1, dsa.DSA_OP_TOPK) == 256 + 4 * 32 * 2048 * 8
+    assert dsa.workspace_size(m1, dsa.DSA_OP_TOPK) == 256 + 4 * 256 * 4 + 4 * 256 * 128 * 8
+    # ... and past 256 rows the two-stage path: 32 segments of 32K keys
+    m1b = Problem(300, 1, 1048576, 1048575, 64, 128, 2048, 128, 512, 64)
+    assert dsa.workspace_size(m1b, dsa.DSA_OP_TOPK) == 300 * 32 * 2048 * 8
     ws = dsa.workspace_size(MLA, dsa.DSA_OP_FORWARD)
     scores = 4096 * 4096 * 4
     idx = 4096 * 2048 * 4
