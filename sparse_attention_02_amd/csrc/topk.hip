@@ -14,10 +14,14 @@
 // equal to it.  Rows held in registers are first cut down to a few thousand
 // candidates with a threshold taken from a sample (see select_top).
 //  * Rows of up to 32768 candidates: one block, keys held in registers (as
-//    16-bit prefixes, two per register, where the row is 16-byte aligned).
-//  * Longer rows: two stages through a workspace (per-segment top k, then the
-//    top k of the segments' candidates), which also spreads a few long rows
-//    (decode) over many blocks.
+//    16-bit prefixes, two per register, where every row fits the candidate
+//    slots and is 16-byte aligned).
+//  * Longer rows, at most 256 of them (decode): a cut taken on a sample of
+//    each row, a filter that keeps the keys at or above it in index order,
+//    and one exact select (topk_sample_cut_kernel, topk_filter_kernel,
+//    topk_cand_kernel).
+//  * Longer rows, more of them: two stages through a workspace (per-segment
+//    top k, then the top k of the segments' candidates).
 //  * Rows beyond that: one block re-reading the row from L2 on each pass.
 #include "dsa_common.h"
 #include "launch.h"
