@@ -381,7 +381,7 @@ int dsa_forward(const dsa_problem* p, const uint8_t* q_idx, const uint8_t* k_idx
  * of 128 MiB that the library holds on every GPU it runs on until the process
  * ends.  Problems whose dsa_workspace_size(p, DSA_OP_FORWARD) exceeds 128 MiB
  * return DSA_ERR_UNSUPPORTED before any launch (the 64-sequence decode over
- * 131,072 tokens needs about 118 MB; long prefills do not fit).  Every call
+ * 131,072 tokens needs about 106 MB; long prefills do not fit).  Every call
  * on a device uses that device's one array: calls that overlap on one device
  * (e.g. on two streams) race and give undefined results.  The first call on a
  * device looks up the array's address there (no allocation).
